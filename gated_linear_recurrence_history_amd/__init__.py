@@ -1,0 +1,12 @@
+"""MI355X-native gated temporal scan (Mamba2-style), forward and backward.
+
+The compute path is the HIP library `libgscan.so` (hand-written gfx950
+kernels behind a C ABI, declared in include/gscan.h); `forward` and
+`backward` are thin ctypes wrappers over it.  There is no CPU fallback.
+"""
+from .binding import (forward, backward, backward_workspace_bytes, library_path,  # noqa: F401
+                      GScanError)
+from . import workloads  # noqa: F401
+
+__all__ = ["forward", "backward", "backward_workspace_bytes", "library_path", "GScanError",
+           "workloads"]

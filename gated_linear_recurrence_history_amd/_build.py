@@ -1,0 +1,63 @@
+"""In-tree build of the package's native libraries.
+
+  libgscan.so        HIP kernels + C ABI (hipcc, gfx950 only)
+  libgscan_synth.so  seeded input generator (gcc + OpenMP)
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+
+HIP_SOURCES = ["gscan_kernels.hip", "gscan_api.hip"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build_synth(verbose: bool = False) -> str:
+    out = os.path.join(PKG, "libgscan_synth.so")
+    tmp = out + ".tmp"
+    _run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+          "-ffp-contract=off", os.path.join(CSRC, "synth.c"), "-o", tmp, "-lm"], verbose)
+    os.replace(tmp, out)
+    return out
+
+
+def build_hip(verbose: bool = False) -> str:
+    out = os.path.join(PKG, "libgscan.so")
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+           # no packed-FP32 instructions anywhere in device code
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument",
+           "-I", INCLUDE, "-I", CSRC]
+    cmd += [os.path.join(CSRC, s) for s in HIP_SOURCES]
+    cmd += ["-o", tmp]
+    _run(cmd, verbose)
+    os.replace(tmp, out)
+    return out
+
+
+def build_all(verbose: bool = False) -> None:
+    build_synth(verbose)
+    build_hip(verbose)
+
+
+if __name__ == "__main__":
+    build_all(verbose=True)

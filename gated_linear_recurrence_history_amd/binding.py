@@ -1,0 +1,158 @@
+"""ctypes binding over libgscan.so (declared in include/gscan.h).
+
+Argument marshalling only: shape/dtype/device checks, raw device pointers and
+the current HIP stream go to the C ABI, every step of the computation runs in
+the library's kernels.  PyTorch provides device memory and streams.  There is
+no fallback: if the library is missing or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgscan.so")
+
+GSCAN_F32 = 0
+GSCAN_BF16 = 1
+
+_lib = None
+
+
+class GScanError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"gscan status {status}: {detail}")
+        self.status = status
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not found: build the HIP library first "
+                               "(__graft_entry__.build()); there is no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+        L.gscan_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp]
+        L.gscan_forward.restype = ctypes.c_int
+        L.gscan_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp,
+                                     vp]
+        L.gscan_backward.restype = ctypes.c_int
+        L.gscan_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp,
+                                       ctypes.c_int, f32, vp]
+        L.gscan_forward_ex.restype = ctypes.c_int
+        L.gscan_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp,
+                                        ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
+        L.gscan_backward_ex.restype = ctypes.c_int
+        L.gscan_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        L.gscan_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.gscan_status_string.argtypes = [ctypes.c_int]
+        L.gscan_status_string.restype = ctypes.c_char_p
+        L.gscan_last_error.argtypes = []
+        L.gscan_last_error.restype = ctypes.c_char_p
+        L.gscan_version.argtypes = []
+        L.gscan_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        detail = lib().gscan_last_error().decode(errors="replace")
+        raise GScanError(status, detail)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return GSCAN_F32
+    if t.dtype == torch.bfloat16:
+        return GSCAN_BF16
+    raise TypeError(f"h_history/h_s2 must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _prep(h_history, h_s2, W_A, W_B, W_C, K):
+    import torch
+    tensors = (h_history, h_s2, W_A, W_B, W_C)
+    dev = h_history.device
+    for t in tensors:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("all operands must be torch tensors on a GPU device")
+        if t.device != dev:
+            raise ValueError("all operands must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("all operands must be contiguous (row-major)")
+    code = _dtype_code(h_history)
+    if h_s2.dtype != h_history.dtype:
+        raise TypeError("h_s2 must have the dtype of h_history")
+    for w in (W_A, W_B, W_C):
+        if w.dtype != torch.float32:
+            raise TypeError("weights must be float32")
+        if w.shape != W_A.shape or w.dim() != 2:
+            raise ValueError("W_A, W_B, W_C must all be [SH2, D]")
+    SH2, D = W_A.shape
+    K = int(K)
+    if K <= 0 or h_history.dim() != 2 or h_history.shape[1] != SH2 or h_history.shape[0] % K:
+        raise ValueError(f"h_history must be [B*K, SH2]; got {tuple(h_history.shape)}, K={K}")
+    B = h_history.shape[0] // K
+    if tuple(h_s2.shape) != (B, SH2):
+        raise ValueError(f"h_s2 must be [B, SH2] = {(B, SH2)}; got {tuple(h_s2.shape)}")
+    return dev, code, B, K, SH2, D
+
+
+def forward(h_history, h_s2, W_A, W_B, W_C, K: int, a_shift: float = 0.0, out=None,
+            stream=None):
+    """context[B, D] (float32) = C * x_K for every (sample, state)."""
+    import torch
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    if out is None:
+        out = torch.empty((B, D), dtype=torch.float32, device=dev)
+    elif out.shape != (B, D) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, D] tensor")
+    _check(lib().gscan_forward_ex(
+        h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
+        W_C.data_ptr(), B, K, SH2, D, out.data_ptr(), code, float(a_shift),
+        _stream_handle(stream, dev)))
+    return out
+
+
+def backward_workspace_bytes(B: int, K: int, SH2: int, D: int, bf16: bool = False) -> int:
+    return int(lib().gscan_backward_workspace_bytes(B, K, SH2, D,
+                                                    GSCAN_BF16 if bf16 else GSCAN_F32))
+
+
+def backward(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: float = 0.0,
+             out=None, workspace=None, stream=None):
+    """(dW_A, dW_B, dW_C), each float32 [SH2, D], for L = sum(d_context * context).
+
+    `workspace` may be a uint8 device tensor of at least backward_workspace_bytes()
+    bytes; otherwise one is taken from torch's caching allocator.
+    """
+    import torch
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    if (not d_context.is_cuda or d_context.dtype != torch.float32
+            or tuple(d_context.shape) != (B, D) or not d_context.is_contiguous()):
+        raise ValueError("d_context must be a contiguous float32 [B, D] GPU tensor")
+    if out is None:
+        out = tuple(torch.empty((SH2, D), dtype=torch.float32, device=dev) for _ in range(3))
+    ws_bytes = int(lib().gscan_backward_workspace_bytes(B, K, SH2, D, code))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().gscan_backward_ex(
+        h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
+        W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), out[0].data_ptr(),
+        out[1].data_ptr(), out[2].data_ptr(), code, float(a_shift), workspace.data_ptr(),
+        workspace.numel(), _stream_handle(stream, dev)))
+    return out

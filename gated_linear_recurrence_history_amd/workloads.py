@@ -1,0 +1,92 @@
+"""Named synthetic workloads and the algorithmic traffic / FLOP model.
+
+Shapes follow the foxhunt design spec "Custom Kernel Optimization - cuBLAS
+Projections + Batch-Parallel Scans": batch 8192 (nsys breakdown table),
+history length K = 8 and hidden width SH2 = 256 (Design 1, "Current"
+paragraph), STATE_D = 16 (Forward Step 1 shapes and the Scratch Buffer
+Requirements table).  The other four workloads widen that shape along K,
+batch, input precision and width.
+
+Distributions: activations ~ N(0, 1), weights ~ N(0, 1/SH2), upstream
+gradient d_context ~ N(0, 1); the long-scan workload adds a constant +2 to
+every A projection before the sigmoid.  The pages give no data, so these
+seeded draws stand in for the trainer's experience buffers.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+# Tensor ids for the counter-based generator, one stream per tensor.
+TID_H_HISTORY = 0
+TID_H_S2 = 1
+TID_W_A = 2
+TID_W_B = 3
+TID_W_C = 4
+TID_D_CONTEXT = 5
+
+SEED_BASE = 20260
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    K: int
+    SH2: int
+    D: int
+    in_dtype: str = "f32"  # "f32" or "bf16": storage type of h_history / h_s2
+    a_shift: float = 0.0
+    seed: int = SEED_BASE
+
+    @property
+    def rows(self) -> int:
+        return self.B * self.K
+
+    @property
+    def in_bytes(self) -> int:
+        return 2 if self.in_dtype == "bf16" else 4
+
+    @property
+    def w_std(self) -> float:
+        return 1.0 / math.sqrt(self.SH2)
+
+    # --- algorithmic traffic: every operand read once, every result written once
+    def fwd_bytes(self) -> int:
+        e = self.in_bytes
+        return (self.rows * self.SH2 * e + self.B * self.SH2 * e
+                + 3 * self.SH2 * self.D * 4 + self.B * self.D * 4)
+
+    def bwd_bytes(self) -> int:
+        e = self.in_bytes
+        return (self.rows * self.SH2 * e + self.B * self.SH2 * e
+                + 3 * self.SH2 * self.D * 4 + self.B * self.D * 4
+                + 3 * self.SH2 * self.D * 4)
+
+    # --- algorithmic multiply-add work (2 FLOP per MAC), scan terms ignored
+    def fwd_flops(self) -> int:
+        return 2 * self.rows * self.SH2 * 2 * self.D + 2 * self.B * self.SH2 * self.D
+
+    def bwd_flops(self) -> int:
+        # replayed projections + the three weight-gradient contractions
+        return 2 * self.fwd_flops()
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "K": self.K, "SH2": self.SH2,
+                "D": self.D, "in_dtype": self.in_dtype, "a_shift": self.a_shift}
+
+
+WORKLOADS = [
+    Workload("tiny_fp32", 64, 8, 256, 16, seed=SEED_BASE + 0),
+    Workload("prod_fp32", 8192, 8, 256, 16, seed=SEED_BASE + 1),
+    Workload("longK_fp32", 8192, 64, 256, 64, a_shift=2.0, seed=SEED_BASE + 2),
+    Workload("bigbatch_bf16", 65536, 8, 256, 16, in_dtype="bf16", seed=SEED_BASE + 3),
+    Workload("wide_fp32", 8192, 256, 512, 128, seed=SEED_BASE + 4),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+HEADLINE = BY_NAME["prod_fp32"]
+
+
+def tolerance(w: Workload) -> float:
+    """Parity tolerance: context max |err| <= tol*(1+|ref|), dW rel-L2 <= tol."""
+    return 2e-2 if w.in_dtype == "bf16" else 1e-4

@@ -1,0 +1,134 @@
+/*
+ * gscan -- gated temporal scan (Mamba2-style), forward and backward, for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (foxhunt design spec "Custom Kernel Optimization - cuBLAS
+ * Projections + Batch-Parallel Scans", Design 1 "Mamba2 Scan"):
+ *
+ *   Forward Step 1:  A = h_history @ W_A (+ a_shift),  Bv = h_history @ W_B,
+ *                    C = h_s2 @ W_C
+ *   Forward Step 2:  per (sample b, state s), x = 0, then for t = 0..K-1
+ *                      x = sigmoid(A[b*K+t, s]) * x + Bv[b*K+t, s]
+ *                    context[b, s] = C[b, s] * x
+ *   Backward Steps 1-3: replay of the forward, reverse scan, and the weight
+ *                    gradients of L = sum(d_context * context):
+ *                      dW_A = h_history^T @ dL/dA,  dW_B = h_history^T @ dL/dBv,
+ *                      dW_C = h_s2^T @ dL/dC   (dL/dC = d_context * x_K)
+ *
+ * Layouts (all dense, row-major, no padding):
+ *   h_history [B*K][SH2]   row b*K + t holds sample b at step t (t = 0 oldest,
+ *                          scanned first)
+ *   h_s2      [B][SH2]
+ *   W_A, W_B, W_C, dW_A, dW_B, dW_C   [SH2][D]   float32
+ *   context, d_context                [B][D]     float32
+ * h_history and h_s2 are float32 (GSCAN_F32) or bfloat16 (GSCAN_BF16, raw
+ * 16-bit storage).  Everything else is float32; all accumulation is float32.
+ *
+ * Supported shapes: B >= 1, K >= 1, 64 <= SH2 <= 512 with SH2 % 64 == 0,
+ * 16 <= D <= 256 with D % 16 == 0, B*K*SH2 < 2^62.
+ *
+ * Pointers: every array pointer is DEVICE memory owned by the caller,
+ * 16-byte aligned.  Inputs are read only and must not overlap outputs.  The
+ * library keeps no allocation between calls.
+ *
+ * Semantics: each call validates its arguments, enqueues its kernels on
+ * `stream` and returns without synchronising; outputs are valid once the
+ * stream reaches that point.  Outputs are overwritten, never accumulated
+ * into.  Results are bitwise reproducible for identical inputs and shapes
+ * (no floating-point atomics).  Calls are reentrant.
+ *
+ * Errors: a non-zero return is one of the GSCAN_ERR_* codes below.  All
+ * argument checks run before anything is enqueued: on a validation error
+ * nothing is launched and no output is touched.  gscan_last_error() gives a
+ * human-readable detail for the calling thread's most recent failure.  NaN
+ * or Inf in the inputs is not an error; it propagates per IEEE-754.
+ */
+#ifndef GSCAN_H
+#define GSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GSCAN_F32 = 0,  /* h_history / h_s2 stored as float32 */
+    GSCAN_BF16 = 1  /* h_history / h_s2 stored as bfloat16 */
+} gscan_dtype_t;
+
+enum {
+    GSCAN_OK = 0,
+    GSCAN_ERR_INVALID_ARGUMENT = 1,  /* null pointer, non-positive size, bad dtype */
+    GSCAN_ERR_UNSUPPORTED_SHAPE = 2, /* shape outside the supported set above */
+    GSCAN_ERR_MISALIGNED = 3,        /* a pointer is not 16-byte aligned */
+    GSCAN_ERR_WORKSPACE_TOO_SMALL = 4,
+    GSCAN_ERR_HIP = 5                /* a HIP runtime call or launch failed */
+};
+
+/*
+ * Forward pass (Forward Steps 1-2): writes context_out[B][D].
+ * Equivalent to gscan_forward_ex(..., GSCAN_F32, 0.0f, stream).
+ */
+int gscan_forward(const void *h_history, const void *h_s2,
+                  const float *W_A, const float *W_B, const float *W_C,
+                  int64_t B, int64_t K, int64_t SH2, int64_t D,
+                  float *context_out, hipStream_t stream);
+
+/*
+ * Backward pass (Backward Steps 1-3): writes dW_A, dW_B, dW_C [SH2][D] for
+ * the upstream gradient d_context[B][D].  Recomputes the forward from the
+ * inputs; needs no saved activations.  Allocates its workspace stream-ordered
+ * (hipMallocAsync / hipFreeAsync on `stream`).
+ * Equivalent to gscan_backward_ex(..., GSCAN_F32, 0.0f, NULL, 0, stream).
+ */
+int gscan_backward(const void *h_history, const void *h_s2,
+                   const float *W_A, const float *W_B, const float *W_C,
+                   int64_t B, int64_t K, int64_t SH2, int64_t D,
+                   const float *d_context, float *dW_A, float *dW_B, float *dW_C,
+                   hipStream_t stream);
+
+/*
+ * Forward with input dtype and gate bias: a_shift is a constant added to
+ * every A value before the sigmoid (it receives no gradient).
+ */
+int gscan_forward_ex(const void *h_history, const void *h_s2,
+                     const float *W_A, const float *W_B, const float *W_C,
+                     int64_t B, int64_t K, int64_t SH2, int64_t D,
+                     float *context_out, gscan_dtype_t in_dtype, float a_shift,
+                     hipStream_t stream);
+
+/*
+ * Backward with input dtype, gate bias and an optional caller workspace.
+ * workspace: device memory of at least gscan_backward_workspace_bytes()
+ * bytes, 256-byte aligned, or NULL to let the call allocate stream-ordered.
+ * The workspace holds per-workgroup weight-gradient partials of the
+ * two-phase reduction; its contents on entry are ignored.
+ */
+int gscan_backward_ex(const void *h_history, const void *h_s2,
+                      const float *W_A, const float *W_B, const float *W_C,
+                      int64_t B, int64_t K, int64_t SH2, int64_t D,
+                      const float *d_context, float *dW_A, float *dW_B, float *dW_C,
+                      gscan_dtype_t in_dtype, float a_shift,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes gscan_backward_ex needs for this shape (0 if unsupported). */
+size_t gscan_backward_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
+                                      gscan_dtype_t in_dtype);
+
+/* Static description of a status code. */
+const char *gscan_status_string(int status);
+
+/* Detail of the calling thread's most recent failure ("" if none). */
+const char *gscan_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gscan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSCAN_H */

@@ -1,0 +1,105 @@
+"""CPU oracle for the gated temporal scan -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package.  The product path (the HIP library and its binding)
+never touches it.
+
+`forward` / `backward` widen every input exactly to float64 (float32 as is,
+bfloat16 given as raw uint16 bits by zero-extending the low mantissa) and
+call plain double-precision C loops (gscan_oracle.c).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        lib = ctypes.CDLL(LIB_PATH)
+        dp = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_forward.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                       ctypes.c_double, dp]
+        lib.oracle_forward.restype = None
+        lib.oracle_backward.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                        ctypes.c_double, dp, dp, dp, dp]
+        lib.oracle_backward.restype = None
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def widen(x: np.ndarray) -> np.ndarray:
+    """Exact widening to float64.  uint16 arrays are raw bfloat16 bits."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        x = (x.astype(np.uint32) << 16).view(np.float32)
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _shapes(h_history, h_s2, W_A, K):
+    SH2, D = W_A.shape
+    B = h_s2.shape[0]
+    if h_history.shape != (B * K, SH2) or h_s2.shape != (B, SH2):
+        raise ValueError(f"shape mismatch: h_history {h_history.shape}, h_s2 {h_s2.shape}, "
+                         f"W {W_A.shape}, K {K}")
+    return B, SH2, D
+
+
+def forward(h_history, h_s2, W_A, W_B, W_C, K: int, a_shift: float = 0.0) -> np.ndarray:
+    """context[B, D] in float64."""
+    h, hs, wa, wb, wc = (widen(a) for a in (h_history, h_s2, W_A, W_B, W_C))
+    B, SH2, D = _shapes(h, hs, wa, K)
+    ctx = np.empty((B, D), dtype=np.float64)
+    _load().oracle_forward(h.ctypes.data, hs.ctypes.data, wa.ctypes.data, wb.ctypes.data,
+                           wc.ctypes.data, B, K, SH2, D, float(a_shift), ctx.ctypes.data)
+    return ctx
+
+
+def backward(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: float = 0.0):
+    """(dW_A, dW_B, dW_C), each [SH2, D] float64, for L = sum(d_context * context)."""
+    h, hs, wa, wb, wc, dc = (widen(a) for a in (h_history, h_s2, W_A, W_B, W_C, d_context))
+    B, SH2, D = _shapes(h, hs, wa, K)
+    if dc.shape != (B, D):
+        raise ValueError(f"d_context shape {dc.shape} != {(B, D)}")
+    dwa = np.empty((SH2, D), dtype=np.float64)
+    dwb = np.empty((SH2, D), dtype=np.float64)
+    dwc = np.empty((SH2, D), dtype=np.float64)
+    _load().oracle_backward(h.ctypes.data, hs.ctypes.data, wa.ctypes.data, wb.ctypes.data,
+                            wc.ctypes.data, B, K, SH2, D, float(a_shift), dc.ctypes.data,
+                            dwa.ctypes.data, dwb.ctypes.data, dwc.ctypes.data)
+    return dwa, dwb, dwc
+
+
+def sample_rows(inputs: dict, K: int, samples) -> dict:
+    """Inputs restricted to the given samples (forward is per-sample independent)."""
+    samples = np.asarray(samples, dtype=np.int64)
+    rows = (samples[:, None] * K + np.arange(K)[None, :]).reshape(-1)
+    out = dict(inputs)
+    out["h_history"] = inputs["h_history"][rows]
+    out["h_s2"] = inputs["h_s2"][samples]
+    if "d_context" in inputs:
+        out["d_context"] = inputs["d_context"][samples]
+    return out

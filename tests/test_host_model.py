@@ -1,0 +1,95 @@
+"""Host-side logic: the seeded generator and the algorithmic traffic model."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from gated_linear_recurrence_history_amd import synth, workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_shapes.json")
+M64 = 2 ** 64 - 1
+
+
+def _splitmix64_reference(state, n):
+    """The published SplitMix64 step, written out for comparison."""
+    outs = []
+    for _ in range(n):
+        state = (state + 0x9E3779B97F4A7C15) & M64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M64
+        outs.append(z ^ (z >> 31))
+    return outs
+
+
+def test_splitmix64_published_first_output():
+    # SplitMix64 seeded with 0 starts 0xE220A8397B1DCDAF.
+    assert synth.splitmix64_first(0) == 0xE220A8397B1DCDAF
+    for st in (1, 12345, 2 ** 63 + 7):
+        assert synth.splitmix64_first(st) == _splitmix64_reference(st, 1)[0]
+
+
+def test_normals_counter_based_and_prefix_stable():
+    a = synth.normal_f32(7, 3, (1000,))
+    b = synth.normal_f32(7, 3, (400,), first=600)
+    assert np.array_equal(a[600:], b)
+    assert not np.array_equal(a, synth.normal_f32(7, 4, (1000,)))
+    assert not np.array_equal(a, synth.normal_f32(8, 3, (1000,)))
+    assert float(a[5]) == np.float32(synth.normal_one(7, 3, 5))
+
+
+def test_normals_moments():
+    x = synth.normal_f32(1, 0, (2_000_000,)).astype(np.float64)
+    assert abs(x.mean()) < 5e-3
+    assert abs(x.std() - 1.0) < 5e-3
+    assert abs(np.mean(x ** 4) - 3.0) < 0.05
+    s = synth.normal_f32(1, 0, (100_000,), stddev=1 / 16).astype(np.float64)
+    assert abs(s.std() - 1 / 16) < 1e-3
+
+
+def test_bf16_round_nearest_even():
+    one = 1.0
+    vals = np.array([one, one + 2 ** -8, one + 3 * 2 ** -8, -2.5, 3.0e38, 1e-40],
+                    dtype=np.float32)
+    bits = synth.round_bf16(vals)
+    back = synth.bf16_bits_to_f32(bits)
+    assert back[0] == 1.0
+    assert back[1] == 1.0                   # tie -> even
+    assert back[2] == 1.0 + 2 ** -6         # tie -> even (up)
+    assert back[3] == -2.5
+    assert np.isfinite(back[4])
+    assert bits.dtype == np.uint16
+
+
+def test_make_inputs_prefix_batch():
+    w = wl.BY_NAME["tiny_fp32"]
+    big = synth.make_inputs(w)
+    small = synth.make_inputs(w, B=10)
+    assert np.array_equal(small["h_history"], big["h_history"][:10 * w.K])
+    assert np.array_equal(small["d_context"], big["d_context"][:10])
+    assert big["W_A"].shape == (w.SH2, w.D)
+    bw = wl.BY_NAME["bigbatch_bf16"]
+    x = synth.make_inputs(bw, B=4)
+    assert x["h_history"].dtype == np.uint16 and x["W_A"].dtype == np.float32
+
+
+def test_traffic_model_matches_page_arithmetic():
+    g = json.load(open(GOLDEN))
+    w = wl.HEADLINE
+    assert (w.B, w.K, w.SH2, w.D) == (g["batch"]["value"], g["K"]["value"], g["SH2"]["value"],
+                                      g["STATE_D"]["value"])
+    assert 3 * w.SH2 * w.D == g["weight_threads"]["value"]
+    old_ops = 3 * w.SH2 * w.D * w.B * w.K * w.SH2
+    assert old_ops == pytest.approx(g["old_backward_ops"]["value"],
+                                    rel=g["old_backward_ops"]["rel_tol"])
+    av = w.rows * w.D * 4
+    assert av == g["A_vals_bytes_MB"]["value"] * 2 ** 20
+    assert w.B * w.D * 4 == g["C_vals_bytes_MB"]["value"] * 2 ** 20
+    scratch = (4 * av + w.B * w.D * 4) / 1e6
+    assert scratch == pytest.approx(g["scratch_total_MB"]["value"],
+                                    rel=g["scratch_total_MB"]["rel_tol"])
+    # our algorithmic model for the headline workload (bytes per pass)
+    assert w.fwd_bytes() == 76_070_912
+    assert w.bwd_bytes() == 76_120_064
+    assert (w.fwd_bytes() + w.bwd_bytes()) // w.B == 18_578

@@ -1,0 +1,74 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case compiles a copy of the oracle's C source with one planted mistake
+(a dropped term, a wrong sign, a wrong index, a transposed operand, a
+reversed time order) into a temporary library and checks that at least one
+pin from test_oracle_pins fails against it.  CPU only; the real oracle is
+untouched.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "gscan_oracle.c")
+
+MUTANTS = {
+    "forward_recurrence_wrong": ("x[s] = g * x[s] + Bv[s];", "x[s] = x[s] + g * Bv[s];"),
+    "dA_drops_state": ("dA[s] = lam[s] * xs[t * D + s] * g * (1.0 - g);",
+                       "dA[s] = lam[s] * g * (1.0 - g);"),
+    "dA_wrong_sign": ("g * (1.0 - g);", "g * (1.0 + g);"),
+    "reverse_drops_gate": ("lam[s] = g * lam[s];", "lam[s] = lam[s];"),
+    "dC_literal_upstream": ("dC[s] = d_context[b * D + s] * xs[K * D + s];",
+                            "dC[s] = d_context[b * D + s];"),
+    "projection_transposed": ("out[s] += row[i] * W[i * D + s];",
+                              "out[s] += row[i] * W[(i * D + s) % SH2 * D + (i * D + s) / SH2];"),
+    "time_reversed": ("const double *row = h_history + (b * K + t) * SH2;\n            project(row, W_A, SH2, D, Av);\n            project(row, W_B, SH2, D, Bv);\n            for (s = 0; s < D; ++s) {\n                const double g = sigmoid(Av[s] + a_shift);\n                x[s]",
+                      "const double *row = h_history + (b * K + (K - 1 - t)) * SH2;\n            project(row, W_A, SH2, D, Av);\n            project(row, W_B, SH2, D, Bv);\n            for (s = 0; s < D; ++s) {\n                const double g = sigmoid(Av[s] + a_shift);\n                x[s]"),
+    "a_shift_ignored": ("sigmoid(Av[s] + a_shift);\n                    gs", "sigmoid(Av[s]);\n                    gs"),
+    "dWC_wrong_row": ("pC[ii * D + s] += h_s2[b * SH2 + ii] * dC[s];",
+                      "pC[ii * D + s] += h_s2[(b + 1) % B * SH2 + ii] * dC[s];"),
+}
+
+
+def _pins():
+    yield lambda: pins.test_gate_zero_closed_form(5, 8, 64, 16)
+    yield lambda: pins.test_constant_gate_geometric_sum(0.9, 8)
+    yield lambda: pins.test_k1_reduces_to_c_times_b(2.0)
+    yield lambda: pins.test_explicit_solution_of_recurrence(2.0, 3, 5, 20, 4)
+    yield lambda: pins.test_euler_homogeneity(2.0)
+    for a in (-3.0, 0.0, 2.0):
+        yield lambda a=a: pins.test_central_finite_differences(a)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mut.c"
+    src.write_text(text.replace(old, new))
+    lib_path = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-fopenmp", str(src), "-o",
+                    str(lib_path), "-lm"], check=True)
+    real = oracle._load()
+    mut = ctypes.CDLL(str(lib_path))
+    for fn in ("oracle_forward", "oracle_backward", "oracle_max_threads", "oracle_set_threads"):
+        getattr(mut, fn).argtypes = getattr(real, fn).argtypes
+        getattr(mut, fn).restype = getattr(real, fn).restype
+    caught = False
+    oracle._lib = mut
+    try:
+        for pin in _pins():
+            try:
+                pin()
+            except AssertionError:
+                caught = True
+                break
+    finally:
+        oracle._lib = real
+    assert caught, f"no pin caught mutant {name}"

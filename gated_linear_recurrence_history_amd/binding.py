@@ -50,6 +50,12 @@ def lib():
         L.gscan_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp,
                                         ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.gscan_backward_ex.restype = ctypes.c_int
+        L.gscan_backward_partials.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp,
+                                              ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
+        L.gscan_backward_partials.restype = ctypes.c_int
+        L.gscan_backward_reduce.argtypes = [vp, ctypes.c_size_t, i64, i64, i64, i64, ctypes.c_int,
+                                            vp, vp, vp, vp]
+        L.gscan_backward_reduce.restype = ctypes.c_int
         L.gscan_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.gscan_backward_workspace_bytes.restype = ctypes.c_size_t
         L.gscan_status_string.argtypes = [ctypes.c_int]
@@ -156,3 +162,75 @@ def backward(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: float =
         out[1].data_ptr(), out[2].data_ptr(), code, float(a_shift), workspace.data_ptr(),
         workspace.numel(), _stream_handle(stream, dev)))
     return out
+
+
+def backward_partials(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, workspace,
+                      a_shift: float = 0.0, stream=None):
+    """Phase 1 of the backward: per-workgroup weight-gradient partials into
+    `workspace` (a uint8 device tensor of at least backward_workspace_bytes())."""
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    _check(lib().gscan_backward_partials(
+        h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(), W_C.data_ptr(),
+        B, K, SH2, D, d_context.data_ptr(), code, float(a_shift), workspace.data_ptr(),
+        workspace.numel(), _stream_handle(stream, dev)))
+
+
+def backward_reduce(workspace, B: int, K: int, SH2: int, D: int, out, bf16: bool = False,
+                    stream=None):
+    """Phase 2 of the backward: fixed-order sum of the partials into out = (dW_A, dW_B, dW_C)."""
+    _check(lib().gscan_backward_reduce(
+        workspace.data_ptr(), workspace.numel(), B, K, SH2, D,
+        GSCAN_BF16 if bf16 else GSCAN_F32, out[0].data_ptr(), out[1].data_ptr(),
+        out[2].data_ptr(), _stream_handle(stream, workspace.device)))
+
+
+class Prepared:
+    """A C-ABI call with its arguments marshalled once (for tight loops: one
+    ctypes call per invocation, no per-call Python checks).  The tensors
+    passed to prepare_* must stay alive while the object is used."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            _check(st)
+
+
+def prepare_forward(h_history, h_s2, W_A, W_B, W_C, K, out, a_shift=0.0, stream=None):
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
+            W_C.data_ptr(), B, K, SH2, D, out.data_ptr(), code, ctypes.c_float(a_shift),
+            _stream_handle(stream, dev))
+    return Prepared(lib().gscan_forward_ex, args, (h_history, h_s2, W_A, W_B, W_C, out))
+
+
+def prepare_backward(h_history, h_s2, W_A, W_B, W_C, K, d_context, out, workspace,
+                     a_shift=0.0, stream=None):
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
+            W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), out[0].data_ptr(),
+            out[1].data_ptr(), out[2].data_ptr(), code, ctypes.c_float(a_shift),
+            workspace.data_ptr(), workspace.numel(), _stream_handle(stream, dev))
+    return Prepared(lib().gscan_backward_ex, args,
+                    (h_history, h_s2, W_A, W_B, W_C, d_context, out, workspace))
+
+
+def prepare_backward_partials(h_history, h_s2, W_A, W_B, W_C, K, d_context, workspace,
+                              a_shift=0.0, stream=None):
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
+            W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), code, ctypes.c_float(a_shift),
+            workspace.data_ptr(), workspace.numel(), _stream_handle(stream, dev))
+    return Prepared(lib().gscan_backward_partials, args,
+                    (h_history, h_s2, W_A, W_B, W_C, d_context, workspace))
+
+
+def prepare_backward_reduce(workspace, B, K, SH2, D, out, bf16=False, stream=None):
+    args = (workspace.data_ptr(), workspace.numel(), B, K, SH2, D,
+            GSCAN_BF16 if bf16 else GSCAN_F32, out[0].data_ptr(), out[1].data_ptr(),
+            out[2].data_ptr(), _stream_handle(stream, workspace.device))
+    return Prepared(lib().gscan_backward_reduce, args, (workspace, out))

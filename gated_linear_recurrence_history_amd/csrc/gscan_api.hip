@@ -1,0 +1,233 @@
+// C ABI of the gated temporal scan (declared in include/gscan.h).
+//
+// Every call validates all arguments before enqueueing anything (the
+// validate-then-launch order of the Kimi-K3 KDA decode launcher page, whose
+// entry point checks every length before its first allocation or launch),
+// returns a status code instead of aborting, and records a detail string in
+// thread-local storage.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gscan.h"
+#include "gscan_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned16(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+int check_common(const void *hh, const void *hs2, const float *WA, const float *WB,
+                 const float *WC, int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype,
+                 gscan::Plan *plan)
+{
+    if (!hh || !hs2 || !WA || !WB || !WC)
+        return fail(GSCAN_ERR_INVALID_ARGUMENT, "null input pointer");
+    if (B <= 0 || K <= 0 || SH2 <= 0 || D <= 0)
+        return fail(GSCAN_ERR_INVALID_ARGUMENT,
+                    "sizes must be positive (B=%lld K=%lld SH2=%lld D=%lld)", (long long)B,
+                    (long long)K, (long long)SH2, (long long)D);
+    if (dtype != GSCAN_F32 && dtype != GSCAN_BF16)
+        return fail(GSCAN_ERR_INVALID_ARGUMENT, "unknown input dtype %d", dtype);
+    if (!gscan::make_plan(B, K, SH2, D, dtype, plan))
+        return fail(GSCAN_ERR_UNSUPPORTED_SHAPE,
+                    "unsupported shape B=%lld K=%lld SH2=%lld D=%lld (need 64<=SH2<=512, "
+                    "SH2%%64==0, 16<=D<=256, D%%16==0)",
+                    (long long)B, (long long)K, (long long)SH2, (long long)D);
+    if (!aligned16(hh) || !aligned16(hs2) || !aligned16(WA) || !aligned16(WB) || !aligned16(WC))
+        return fail(GSCAN_ERR_MISALIGNED, "input pointers must be 16-byte aligned");
+    return GSCAN_OK;
+}
+
+int check_backward(const void *h_history, const void *h_s2, const float *W_A, const float *W_B,
+                   const float *W_C, int64_t B, int64_t K, int64_t SH2, int64_t D,
+                   const float *d_context, int dtype, gscan::Plan *plan)
+{
+    int st = check_common(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, dtype, plan);
+    if (st != GSCAN_OK) return st;
+    if (!d_context) return fail(GSCAN_ERR_INVALID_ARGUMENT, "null d_context");
+    if (!aligned16(d_context))
+        return fail(GSCAN_ERR_MISALIGNED, "d_context must be 16-byte aligned");
+    return GSCAN_OK;
+}
+
+int check_outputs(const float *dW_A, const float *dW_B, const float *dW_C)
+{
+    if (!dW_A || !dW_B || !dW_C) return fail(GSCAN_ERR_INVALID_ARGUMENT, "null dW pointer");
+    if (!aligned16(dW_A) || !aligned16(dW_B) || !aligned16(dW_C))
+        return fail(GSCAN_ERR_MISALIGNED, "dW pointers must be 16-byte aligned");
+    return GSCAN_OK;
+}
+
+int check_workspace(const void *workspace, size_t workspace_bytes, const gscan::Plan &plan)
+{
+    if (!workspace) return fail(GSCAN_ERR_INVALID_ARGUMENT, "null workspace");
+    if (workspace_bytes < plan.ws_bytes)
+        return fail(GSCAN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu",
+                    workspace_bytes, plan.ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(GSCAN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    return GSCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gscan_forward_ex(const void *h_history, const void *h_s2, const float *W_A, const float *W_B,
+                     const float *W_C, int64_t B, int64_t K, int64_t SH2, int64_t D,
+                     float *context_out, gscan_dtype_t in_dtype, float a_shift,
+                     hipStream_t stream)
+{
+    gscan::Plan plan;
+    int st = check_common(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, (int)in_dtype, &plan);
+    if (st != GSCAN_OK) return st;
+    if (!context_out) return fail(GSCAN_ERR_INVALID_ARGUMENT, "null context_out");
+    if (!aligned16(context_out))
+        return fail(GSCAN_ERR_MISALIGNED, "context_out must be 16-byte aligned");
+    hipError_t e = gscan::launch_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
+                                         context_out, stream);
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return GSCAN_OK;
+}
+
+int gscan_forward(const void *h_history, const void *h_s2, const float *W_A, const float *W_B,
+                  const float *W_C, int64_t B, int64_t K, int64_t SH2, int64_t D,
+                  float *context_out, hipStream_t stream)
+{
+    return gscan_forward_ex(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, context_out, GSCAN_F32,
+                            0.0f, stream);
+}
+
+size_t gscan_backward_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
+                                      gscan_dtype_t in_dtype)
+{
+    gscan::Plan plan;
+    if (!gscan::make_plan(B, K, SH2, D, (int)in_dtype, &plan)) return 0;
+    return plan.ws_bytes;
+}
+
+int gscan_backward_ex(const void *h_history, const void *h_s2, const float *W_A,
+                      const float *W_B, const float *W_C, int64_t B, int64_t K, int64_t SH2,
+                      int64_t D, const float *d_context, float *dW_A, float *dW_B, float *dW_C,
+                      gscan_dtype_t in_dtype, float a_shift, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream)
+{
+    gscan::Plan plan;
+    int st = check_backward(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, d_context,
+                            (int)in_dtype, &plan);
+    if (st != GSCAN_OK) return st;
+    if ((st = check_outputs(dW_A, dW_B, dW_C)) != GSCAN_OK) return st;
+    if (workspace && (st = check_workspace(workspace, workspace_bytes, plan)) != GSCAN_OK)
+        return st;
+    void *ws = workspace;
+    if (!ws) {
+        hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, stream);
+        if (e != hipSuccess)
+            return fail(GSCAN_ERR_HIP, "workspace allocation of %zu bytes failed: %s",
+                        plan.ws_bytes, hipGetErrorString(e));
+    }
+    float *part = static_cast<float *>(ws);
+    hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
+                                                   d_context, part, stream);
+    if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
+    if (!workspace) {
+        hipError_t f = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = f;
+    }
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return GSCAN_OK;
+}
+
+int gscan_backward_partials(const void *h_history, const void *h_s2, const float *W_A,
+                            const float *W_B, const float *W_C, int64_t B, int64_t K,
+                            int64_t SH2, int64_t D, const float *d_context,
+                            gscan_dtype_t in_dtype, float a_shift, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream)
+{
+    gscan::Plan plan;
+    int st = check_backward(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, d_context,
+                            (int)in_dtype, &plan);
+    if (st != GSCAN_OK) return st;
+    if ((st = check_workspace(workspace, workspace_bytes, plan)) != GSCAN_OK) return st;
+    hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
+                                                   d_context, static_cast<float *>(workspace),
+                                                   stream);
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "backward phase 1 launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return GSCAN_OK;
+}
+
+int gscan_backward_reduce(const void *workspace, size_t workspace_bytes, int64_t B, int64_t K,
+                          int64_t SH2, int64_t D, gscan_dtype_t in_dtype, float *dW_A,
+                          float *dW_B, float *dW_C, hipStream_t stream)
+{
+    gscan::Plan plan;
+    if (B <= 0 || K <= 0 || SH2 <= 0 || D <= 0)
+        return fail(GSCAN_ERR_INVALID_ARGUMENT, "sizes must be positive");
+    if (in_dtype != GSCAN_F32 && in_dtype != GSCAN_BF16)
+        return fail(GSCAN_ERR_INVALID_ARGUMENT, "unknown input dtype %d", (int)in_dtype);
+    if (!gscan::make_plan(B, K, SH2, D, (int)in_dtype, &plan))
+        return fail(GSCAN_ERR_UNSUPPORTED_SHAPE, "unsupported shape");
+    int st;
+    if ((st = check_workspace(workspace, workspace_bytes, plan)) != GSCAN_OK) return st;
+    if ((st = check_outputs(dW_A, dW_B, dW_C)) != GSCAN_OK) return st;
+    hipError_t e = gscan::launch_backward_reduce(plan, static_cast<const float *>(workspace), dW_A,
+                                                 dW_B, dW_C, stream);
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "backward phase 2 launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return GSCAN_OK;
+}
+
+int gscan_backward(const void *h_history, const void *h_s2, const float *W_A, const float *W_B,
+                   const float *W_C, int64_t B, int64_t K, int64_t SH2, int64_t D,
+                   const float *d_context, float *dW_A, float *dW_B, float *dW_C,
+                   hipStream_t stream)
+{
+    return gscan_backward_ex(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, d_context, dW_A, dW_B,
+                             dW_C, GSCAN_F32, 0.0f, nullptr, 0, stream);
+}
+
+const char *gscan_status_string(int status)
+{
+    switch (status) {
+    case GSCAN_OK: return "ok";
+    case GSCAN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case GSCAN_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case GSCAN_ERR_MISALIGNED: return "misaligned pointer";
+    case GSCAN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case GSCAN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *gscan_last_error(void)
+{
+    return g_last_error;
+}
+
+int gscan_version(void)
+{
+    return 100;  // 0.1.0
+}
+
+}  // extern "C"

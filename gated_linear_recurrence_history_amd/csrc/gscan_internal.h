@@ -1,0 +1,54 @@
+// Internal interface between the C ABI (gscan_api.hip) and the kernels
+// (gscan_kernels.hip).  The launch plan is pure host arithmetic.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+namespace gscan {
+
+// Work decomposition shared by every kernel.
+constexpr int kWave = 64;          // lanes per wavefront
+constexpr int kWaves = 4;          // wavefronts per workgroup
+constexpr int kThreads = kWave * kWaves;
+constexpr int kGroupSamples = 16;  // samples per workgroup work item
+constexpr int kSlice = 16;         // states per workgroup (one MFMA N tile)
+constexpr int kBlockRows = 16;     // h_history rows per wavefront block (MFMA M tile)
+constexpr int kChunkRows = kBlockRows * kWaves;  // rows per backward chunk
+constexpr int kXcds = 8;           // MI355X accelerator complex dies
+constexpr int kMaxSH2 = 512;
+constexpr int kMaxD = 256;
+
+struct Plan {
+    int64_t B = 0, K = 0, SH2 = 0, D = 0;
+    int dtype = 0;          // 0 f32, 1 bf16
+    int nq = 0;             // SH2 / 32
+    int slices = 0;         // D / 16
+    int64_t groups = 0;     // ceil(B / 16)
+    int64_t fwd_rows = 0;   // group slots of the forward grid (multiple of 8)
+    int64_t bwd_rows = 0;   // persistent workgroup rows of the backward grid (multiple of 8)
+    int64_t fwd_grid = 0;
+    int64_t bwd_grid = 0;
+    int64_t red_grid = 0;
+    size_t ws_bytes = 0;    // weight-gradient partials: bwd_rows x 3 x SH2 x D floats
+};
+
+// Fills `p` for a validated shape.  Returns false if the shape is unsupported.
+bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p);
+
+hipError_t launch_forward(const Plan &p, const void *h_history, const void *h_s2,
+                          const float *W_A, const float *W_B, const float *W_C,
+                          float a_shift, float *context, hipStream_t stream);
+
+// Phase 1: per-workgroup weight-gradient partials into `partials`.
+hipError_t launch_backward_partials(const Plan &p, const void *h_history, const void *h_s2,
+                                    const float *W_A, const float *W_B, const float *W_C,
+                                    float a_shift, const float *d_context, float *partials,
+                                    hipStream_t stream);
+
+// Phase 2: fixed-order sum of the partials into dW_A, dW_B, dW_C.
+hipError_t launch_backward_reduce(const Plan &p, const float *partials, float *dW_A,
+                                  float *dW_B, float *dW_C, hipStream_t stream);
+
+}  // namespace gscan

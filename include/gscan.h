@@ -114,6 +114,30 @@ int gscan_backward_ex(const void *h_history, const void *h_s2,
                       gscan_dtype_t in_dtype, float a_shift,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The two phases of gscan_backward_ex, callable separately (for example to
+ * time them, or to run the reduction later on the same stream):
+ *
+ * Phase 1 writes one weight-gradient partial per backward workgroup into
+ * `workspace` (required here, at least gscan_backward_workspace_bytes(),
+ * 256-byte aligned).  Phase 2 sums those partials in a fixed order -- so the
+ * result is bitwise reproducible -- and overwrites dW_A, dW_B, dW_C.  Phase 2
+ * must see the same shape and dtype as the phase 1 that filled the workspace.
+ * This is the two-phase batch-parallel reduction of the design spec (section
+ * "IQN Bias Grad Reduce": block partials, then a reduction of the partials)
+ * applied to the weight gradients.
+ */
+int gscan_backward_partials(const void *h_history, const void *h_s2,
+                            const float *W_A, const float *W_B, const float *W_C,
+                            int64_t B, int64_t K, int64_t SH2, int64_t D,
+                            const float *d_context, gscan_dtype_t in_dtype, float a_shift,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+int gscan_backward_reduce(const void *workspace, size_t workspace_bytes,
+                          int64_t B, int64_t K, int64_t SH2, int64_t D,
+                          gscan_dtype_t in_dtype, float *dW_A, float *dW_B, float *dW_C,
+                          hipStream_t stream);
+
 /* Workspace bytes gscan_backward_ex needs for this shape (0 if unsupported). */
 size_t gscan_backward_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
                                       gscan_dtype_t in_dtype);

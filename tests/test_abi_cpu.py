@@ -1,0 +1,106 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/gscan.h declares, and rejects bad arguments before any launch.
+
+Only validation paths are exercised (every call here fails its checks before
+anything is enqueued), so no HIP device is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_linear_recurrence_history_amd import binding, workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gscan.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4, 5
+FAKE = 0x10000  # aligned non-null "device pointer"; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from gated_linear_recurrence_history_amd import _build
+        _build.build_hip()
+    return binding.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gscan_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert {"gscan_forward", "gscan_backward", "gscan_forward_ex", "gscan_backward_ex",
+            "gscan_backward_workspace_bytes", "gscan_status_string", "gscan_backward_partials", "gscan_backward_reduce",
+            "gscan_last_error", "gscan_version"} <= set(names)
+    raw = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in gscan.h but not exported"
+
+
+def test_status_strings(lib):
+    for code, text in [(OK, b"ok"), (INVALID, b"invalid argument"),
+                       (UNSUPPORTED, b"unsupported shape"), (MISALIGNED, b"misaligned pointer"),
+                       (WS_SMALL, b"workspace too small"), (HIPERR, b"HIP runtime error")]:
+        assert lib.gscan_status_string(code) == text
+    assert lib.gscan_status_string(99) == b"unknown status"
+    assert lib.gscan_version() >= 100
+
+
+def test_workspace_bytes(lib):
+    w = wl.HEADLINE
+    n = lib.gscan_backward_workspace_bytes(w.B, w.K, w.SH2, w.D, 0)
+    per = 3 * w.SH2 * w.D * 4
+    assert n > 0 and n % per == 0 and (n // per) % 8 == 0
+    assert lib.gscan_backward_workspace_bytes(w.B, w.K, 100, w.D, 0) == 0
+    assert lib.gscan_backward_workspace_bytes(w.B, w.K, w.SH2, 24, 0) == 0
+    assert lib.gscan_backward_workspace_bytes(w.B, w.K, w.SH2, w.D, 7) == 0
+    for cfg in wl.WORKLOADS:
+        assert lib.gscan_backward_workspace_bytes(cfg.B, cfg.K, cfg.SH2, cfg.D,
+                                                  1 if cfg.in_dtype == "bf16" else 0) > 0
+
+
+def _fwd(lib, hh=FAKE, hs=FAKE, wa=FAKE, wb=FAKE, wc=FAKE, B=64, K=8, SH2=256, D=16, out=FAKE,
+         dtype=0):
+    return lib.gscan_forward_ex(hh, hs, wa, wb, wc, B, K, SH2, D, out, dtype, 0.0, None)
+
+
+def _bwd(lib, B=64, K=8, SH2=256, D=16, dctx=FAKE, dwa=FAKE, ws=None, ws_bytes=0, dtype=0,
+         hh=FAKE):
+    return lib.gscan_backward_ex(hh, FAKE, FAKE, FAKE, FAKE, B, K, SH2, D, dctx, dwa, FAKE,
+                                 FAKE, dtype, 0.0, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hh=None), INVALID), (dict(wc=None), INVALID), (dict(out=None), INVALID),
+    (dict(B=0), INVALID), (dict(K=-1), INVALID), (dict(SH2=0), INVALID), (dict(dtype=3), INVALID),
+    (dict(SH2=96), UNSUPPORTED), (dict(SH2=1024), UNSUPPORTED), (dict(D=8), UNSUPPORTED),
+    (dict(D=24), UNSUPPORTED), (dict(D=272), UNSUPPORTED),
+    (dict(hh=FAKE + 4), MISALIGNED), (dict(out=FAKE + 8), MISALIGNED),
+])
+def test_forward_validation(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+    assert lib.gscan_last_error() != b""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dctx=None), INVALID), (dict(dwa=None), INVALID), (dict(hh=None), INVALID),
+    (dict(D=17), UNSUPPORTED), (dict(dctx=FAKE + 4), MISALIGNED),
+    (dict(ws=FAKE, ws_bytes=16), WS_SMALL),
+    (dict(ws=FAKE + 16, ws_bytes=1 << 40), MISALIGNED),
+])
+def test_backward_validation(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+    assert lib.gscan_last_error() != b""
+
+
+def test_plain_entry_points_validate(lib):
+    assert lib.gscan_forward(None, FAKE, FAKE, FAKE, FAKE, 64, 8, 256, 16, FAKE, None) == INVALID
+    assert lib.gscan_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 8, 256, 12, FAKE, FAKE, FAKE,
+                              FAKE, None) == UNSUPPORTED
+    assert b"unsupported shape" in lib.gscan_last_error()

@@ -1,0 +1,94 @@
+"""GPU behaviour beyond parity: bitwise reproducibility, isolation of
+non-finite values between samples, stream and workspace variants, and error
+reporting through the binding."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import gated_linear_recurrence_history_amd as gs
+from gated_linear_recurrence_history_amd import binding, synth, workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_util import DEV, device_inputs, gpu_backward, gpu_forward, workload  # noqa: E402
+
+
+def test_bitwise_reproducible():
+    w = wl.HEADLINE
+    print(f"case reproducible {w.name}", flush=True)
+    t = device_inputs(synth.make_inputs(w))
+    c1 = gpu_forward(t, w.K, 0.0)
+    c2 = gpu_forward(t, w.K, 0.0)
+    assert np.array_equal(c1, c2)
+    g1 = gpu_backward(t, w.K, 0.0)
+    g2 = gpu_backward(t, w.K, 0.0)
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("K", [8, 5, 70])
+def test_non_finite_stays_in_its_sample(K):
+    w = workload(40, K, 128, 32, seed=5)
+    print(f"case nonfinite K={K}", flush=True)
+    x = synth.make_inputs(w)
+    clean = gpu_forward(device_inputs(x), K, 0.0)
+    y = {k: v.copy() for k, v in x.items()}
+    y["h_history"][5 * K + K // 2, 3] = np.nan        # sample 5
+    y["h_history"][17 * K, 0] = np.inf                # sample 17, first step
+    y["h_s2"][30, 7] = -np.inf                        # sample 30
+    dirty = gpu_forward(device_inputs(y), K, 0.0)
+    bad = {5, 17, 30}
+    for b in range(w.B):
+        if b in bad:
+            assert not np.all(np.isfinite(dirty[b])), b
+        else:
+            assert np.array_equal(dirty[b], clean[b]), b
+    dW = gpu_backward(device_inputs(y), K, 0.0)
+    assert all(not np.all(np.isfinite(g)) for g in dW[:2])
+
+
+def test_plain_entry_points_and_streams():
+    w = workload(300, 8, 256, 32, seed=9)
+    print("case plain/ex/stream", flush=True)
+    x = synth.make_inputs(w)
+    t = device_inputs(x)
+    ref_ctx = gpu_forward(t, w.K, 0.0)
+    ref_dW = gpu_backward(t, w.K, 0.0)
+    L = binding.lib()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ctx = torch.full((w.B, w.D), 7.0, device=DEV)
+        dW = [torch.full((w.SH2, w.D), 7.0, device=DEV) for _ in range(3)]
+        h = ctypes.c_void_p(s.cuda_stream)
+        assert L.gscan_forward(t["h_history"].data_ptr(), t["h_s2"].data_ptr(),
+                               t["W_A"].data_ptr(), t["W_B"].data_ptr(), t["W_C"].data_ptr(),
+                               w.B, w.K, w.SH2, w.D, ctx.data_ptr(), h) == 0
+        assert L.gscan_backward(t["h_history"].data_ptr(), t["h_s2"].data_ptr(),
+                                t["W_A"].data_ptr(), t["W_B"].data_ptr(), t["W_C"].data_ptr(),
+                                w.B, w.K, w.SH2, w.D, t["d_context"].data_ptr(),
+                                dW[0].data_ptr(), dW[1].data_ptr(), dW[2].data_ptr(), h) == 0
+    s.synchronize()
+    assert np.array_equal(ctx.cpu().numpy(), ref_ctx)
+    for a, b in zip(dW, ref_dW):
+        assert np.array_equal(a.cpu().numpy(), b)
+
+
+def test_errors_leave_outputs_untouched():
+    w = workload(32, 8, 256, 16, seed=3)
+    t = device_inputs(synth.make_inputs(w))
+    out = torch.full((w.B, w.D), 3.0, device=DEV)
+    bad_W = torch.zeros((w.SH2, 24), device=DEV)  # D = 24 is not a multiple of 16
+    bad_h = torch.zeros((w.B * w.K, 24), device=DEV)
+    with pytest.raises(gs.GScanError) as ei:
+        L = binding.lib()
+        st = L.gscan_forward_ex(t["h_history"].data_ptr(), t["h_s2"].data_ptr(),
+                                bad_W.data_ptr(), bad_W.data_ptr(), bad_W.data_ptr(), w.B, w.K,
+                                w.SH2, 24, out.data_ptr(), 0, 0.0, None)
+        binding._check(st)
+    assert ei.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+    with pytest.raises(ValueError):
+        gs.forward(bad_h, t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K)

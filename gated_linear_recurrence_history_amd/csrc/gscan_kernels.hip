@@ -16,15 +16,23 @@
 // backward contracts the gradients on chip into per-workgroup partials that
 // a second small kernel sums in a fixed order (no floating-point atomics).
 //
+// Arithmetic.  Products of h with W (projections) and of h with dL/dA, dL/dBv
+// (weight gradients) run on bf16 MFMA with a two-term split of each fp32
+// operand, x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (both round to
+// nearest even), keeping hi*hi + hi*lo + lo*hi and accumulating in fp32.
+// The dropped terms are below 2^-16 of each product.  bf16 inputs are exact
+// in hi, so their lo term vanishes and is skipped.  dW_C, the only contraction
+// over samples rather than rows, uses fp32 MFMA.
+//
 // Work decomposition
 //   workgroup = 4 wavefronts = one "group" of 16 samples x one 16-state slice
-//   of D.  The weight slice [SH2 x (16 A | 16 B | 16 C)] is staged in LDS in
-//   MFMA operand order.  MFMA v_mfma_f32_16x16x4_f32: for a 16-row block of
-//   h_history, lane l holds row (l % 16) and eight consecutive columns
-//   32q + 8(l/16) + e of every 32-column unit q; the contraction order over
-//   SH2 is a permutation applied identically to h and W, so 16-byte loads
-//   feed the A operand directly.  The 16x16 result gives lane l the state
-//   s = l % 16 for rows 4(l/16) + j, j = 0..3.
+//   of D.  The weight slice [SH2 x (16 A | 16 B | 16 C)] is split into bf16
+//   hi/lo and staged in LDS in MFMA operand order.  For MFMA
+//   v_mfma_f32_16x16x32_bf16 on a 16-row block of h_history, lane l holds row
+//   l % 16 and the eight consecutive columns 32q + 8(l/16) + e of every
+//   32-column unit q; the contraction order over SH2 is a permutation applied
+//   identically to h and W, so 16-byte row loads feed the operand directly.
+//   The 16x16 result gives lane l the state s = l % 16 for rows 4(l/16) + j.
 //
 // Scan on that layout: every row is an affine map of the state,
 //   x -> g*x + b          (t > 0)
@@ -42,11 +50,9 @@ namespace gscan {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f4 mfma(float a, float b, f4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f4 zero4()
 {
@@ -54,39 +60,116 @@ __device__ __forceinline__ f4 zero4()
     return z;
 }
 
-// ---------------------------------------------------------------- input loads
-template <typename T> struct In;
+__device__ __forceinline__ u4 zero_u4()
+{
+    u4 z = {0u, 0u, 0u, 0u};
+    return z;
+}
 
-template <> struct In<float> {
-    // eight consecutive columns starting at p (16-byte aligned)
-    static __device__ __forceinline__ void load8(const float *p, float (&v)[8])
-    {
-        const f4 a = *reinterpret_cast<const f4 *>(p);
-        const f4 b = *reinterpret_cast<const f4 *>(p + 4);
-        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-        v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+// fp32 MFMA 16x16x4 (A: lane l -> row l%16, k l/16; B: k l/16, column l%16)
+__device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// bf16 MFMA 16x16x32 (A: lane l -> row l%16, k 8(l/16)+e; B: k 8(l/16)+e, column l%16)
+__device__ __forceinline__ f4 mfma_bf(u4 a, u4 b, f4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// two floats -> packed bf16 pair (round to nearest even), first in the low half
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
+{
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// x = hi + lo for eight values (packed eight bf16 per u4)
+struct Split {
+    u4 hi, lo;
+};
+
+__device__ __forceinline__ Split split8(const float (&v)[8])
+{
+    Split s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h = pack_bf16(v[2 * i], v[2 * i + 1]);
+        s.hi[i] = h;
+        s.lo[i] = pack_bf16(v[2 * i] - bf_lo(h), v[2 * i + 1] - bf_hi(h));
     }
-    static __device__ __forceinline__ f4 load4(const float *p)
+    return s;
+}
+
+// c += a * b with both operands split; LO_A = false when a is exact in bf16
+template <bool LO_A>
+__device__ __forceinline__ f4 mfma3(const Split &a, const Split &b, f4 c)
+{
+    c = mfma_bf(a.hi, b.lo, c);
+    if (LO_A) c = mfma_bf(a.lo, b.hi, c);
+    return mfma_bf(a.hi, b.hi, c);
+}
+
+// ---------------------------------------------------------------- input rows
+// Projection ("P") layout of one 16-row block: lane l, unit q -> row l%16,
+// columns 32q + 8(l/16) + 0..7.
+template <typename T, int NQ> struct PBlk;
+
+template <int NQ> struct PBlk<float, NQ> {
+    static constexpr bool kLo = true;
+    f4 v[NQ][2];
+    __device__ __forceinline__ void load(const float *__restrict__ row, int kg)
     {
-        return *reinterpret_cast<const f4 *>(p);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            v[q][0] = *reinterpret_cast<const f4 *>(row + 32 * q + 8 * kg);
+            v[q][1] = *reinterpret_cast<const f4 *>(row + 32 * q + 8 * kg + 4);
+        }
+    }
+    __device__ __forceinline__ Split op(int q) const
+    {
+        float x[8] = {v[q][0][0], v[q][0][1], v[q][0][2], v[q][0][3],
+                      v[q][1][0], v[q][1][1], v[q][1][2], v[q][1][3]};
+        return split8(x);
     }
 };
 
-// bfloat16 storage: widening is exact (the value's bits are the top half of a float)
-template <> struct In<uint16_t> {
-    static __device__ __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
-    static __device__ __forceinline__ float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-    static __device__ __forceinline__ void load8(const uint16_t *p, float (&v)[8])
+template <int NQ> struct PBlk<uint16_t, NQ> {
+    static constexpr bool kLo = false;  // bf16 storage is exact in hi
+    u4 v[NQ];
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ row, int kg)
     {
-        const uint4 u = *reinterpret_cast<const uint4 *>(p);
-        v[0] = lo(u.x); v[1] = hi(u.x); v[2] = lo(u.y); v[3] = hi(u.y);
-        v[4] = lo(u.z); v[5] = hi(u.z); v[6] = lo(u.w); v[7] = hi(u.w);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) v[q] = *reinterpret_cast<const u4 *>(row + 32 * q + 8 * kg);
     }
-    static __device__ __forceinline__ f4 load4(const uint16_t *p)
+    __device__ __forceinline__ Split op(int q) const
+    {
+        Split s;
+        s.hi = v[q];
+        s.lo = zero_u4();
+        return s;
+    }
+};
+
+// four consecutive columns of one row as float (transposed "T" layout loads)
+template <typename T> struct Col4;
+template <> struct Col4<float> {
+    static __device__ __forceinline__ f4 load(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+};
+template <> struct Col4<uint16_t> {
+    static __device__ __forceinline__ f4 load(const uint16_t *p)
     {
         const uint2 u = *reinterpret_cast<const uint2 *>(p);
         f4 r;
-        r[0] = lo(u.x); r[1] = hi(u.x); r[2] = lo(u.y); r[3] = hi(u.y);
+        r[0] = bf_lo(u.x);
+        r[1] = bf_hi(u.x);
+        r[2] = bf_lo(u.y);
+        r[3] = bf_hi(u.y);
         return r;
     }
 };
@@ -128,8 +211,8 @@ __device__ __forceinline__ Aff shfl_aff(const Aff &a, int src)
     return o;
 }
 
-// Prefix over the four lane groups g = lane/16 (ascending): returns the
-// composite of groups < g (exclusive) and of all four groups (total).
+// Prefix over the four lane groups g = lane/16 (ascending): the composite of
+// groups < g (exclusive) and of all four groups (total).
 __device__ __forceinline__ void scan_up(const Aff &mine, int lane, Aff &excl, Aff &total)
 {
     const int kg = lane >> 4;
@@ -166,85 +249,160 @@ __device__ __forceinline__ float sigmoid(float a)
     return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
-// --------------------------------------------------------------- weight slice
-// LDS image of [W_A | W_B | W_C][:, s0 .. s0+16) in MFMA B-operand order:
-// entry ((q*3 + w)*2 + half)*64 + lane holds, for state s0 + lane%16,
-// the four rows 32q + 8(lane/16) + 4*half + {0..3} of weight w.
-template <int NQ>
-__device__ __forceinline__ void stage_weights(f4 *Wl, const float *__restrict__ WA,
-                                              const float *__restrict__ WB,
-                                              const float *__restrict__ WC, int D, int s0)
+// ------------------------------------------------------------ row bookkeeping
+// A lane's four rows in a block are base + 4*(l/16) + j, j = 0..3, with base
+// uniform across the wavefront.  (sample, step) = divmod(row, K) is formed
+// from divmod(base, K) (one uniform division) and the lane's fixed offsets
+// divmod(4*(l/16) + j, K) (computed once), so no per-row division is needed.
+struct LaneOff {
+    int ob[4], ot[4];
+};
+
+__device__ __forceinline__ LaneOff lane_offsets(int kg, int K)
 {
-    for (int idx = threadIdx.x; idx < NQ * 3 * 2 * kWave; idx += kThreads) {
-        const int ln = idx & 63;
-        int rest = idx >> 6;
-        const int half = rest & 1;
-        rest >>= 1;
-        const int w = rest % 3;
-        const int q = rest / 3;
-        const int k0 = 32 * q + 8 * (ln >> 4) + 4 * half;
-        const int s = s0 + (ln & 15);
-        const float *W = w == 0 ? WA : (w == 1 ? WB : WC);
-        f4 v;
-        v[0] = W[(k0 + 0) * D + s];
-        v[1] = W[(k0 + 1) * D + s];
-        v[2] = W[(k0 + 2) * D + s];
-        v[3] = W[(k0 + 3) * D + s];
-        Wl[idx] = v;
+    LaneOff o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int v = 4 * kg + j;
+        o.ob[j] = v / K;
+        o.ot[j] = v - o.ob[j] * K;
     }
+    return o;
 }
 
-__device__ __forceinline__ const f4 &wop(const f4 *Wl, int q, int w, int half, int lane)
+struct RowPos {
+    int bl, t;
+};
+
+// divmod of a wavefront-uniform value
+__device__ __forceinline__ RowPos base_pos(int base, int K)
 {
-    return Wl[((q * 3 + w) * 2 + half) * kWave + lane];
+    const int b = __builtin_amdgcn_readfirstlane(base / K);
+    RowPos p = {b, base - b * K};
+    return p;
 }
 
-// A|Bv projection of one 16-row block: `rowp` is this lane's row (row l%16).
-template <typename TIn, int NQ>
-__device__ __forceinline__ void project_block(const TIn *__restrict__ rowp, const f4 *Wl, int lane,
-                                              f4 &aA, f4 &aB)
+__device__ __forceinline__ RowPos row_pos(const RowPos &bp, const LaneOff &lo, int j, int K)
 {
-    const int kg = lane >> 4;
-    float hv[NQ][8];
+    RowPos p = {bp.bl + lo.ob[j], bp.t + lo.ot[j]};
+    if (p.t >= K) {
+        p.t -= K;
+        ++p.bl;
+    }
+    return p;
+}
+
+__device__ __forceinline__ int wave_id()
+{
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// --------------------------------------------------------------- weight slice
+// LDS image of [W_A | W_B | W_C][:, s0 .. s0+16) as bf16 hi/lo in MFMA
+// B-operand order: entry ((q*3 + w)*2 + part)*64 + lane holds rows
+// 32q + 8(lane/16) + 0..7 of weight w for state s0 + lane%16.
+// Loaded into registers first (so the loads are in flight early), then
+// split and stored.
+template <int NQ>
+struct WStage {
+    static constexpr int kEntries = NQ * 3 * kWave;
+    static constexpr int kPer = (kEntries + kThreads - 1) / kThreads;
+    float v[kPer][8];
+
+    __device__ __forceinline__ void load(const float *__restrict__ WA, const float *__restrict__ WB,
+                                         const float *__restrict__ WC, int D, int s0)
+    {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) In<TIn>::load8(rowp + 32 * q + 8 * kg, hv[q]);
-    aA = zero4();
-    aB = zero4();
+        for (int i = 0; i < kPer; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            if (idx < kEntries) {
+                const int ln = idx & 63;
+                const int rest = idx >> 6;
+                const int w = rest % 3;
+                const int q = rest / 3;
+                const float *W = w == 0 ? WA : (w == 1 ? WB : WC);
+                const float *p = W + (32 * q + 8 * (ln >> 4)) * D + s0 + (ln & 15);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const f4 wa = wop(Wl, q, 0, half, lane);
-            const f4 wb = wop(Wl, q, 1, half, lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                aA = mfma(hv[q][4 * half + e], wa[e], aA);
-                aB = mfma(hv[q][4 * half + e], wb[e], aB);
+                for (int e = 0; e < 8; ++e) v[i][e] = p[e * D];
             }
         }
     }
-}
-
-// C projection partial over the 32-column units q = wave, wave+4, ... for the
-// group's 16 samples (row l%16 = sample).
-template <typename TIn, int NQ>
-__device__ __forceinline__ f4 project_c_partial(const TIn *__restrict__ rowp, const f4 *Wl,
-                                                int lane, int wave)
-{
-    const int kg = lane >> 4;
-    f4 acc = zero4();
-    for (int q = wave; q < NQ; q += kWaves) {
-        float hv[8];
-        In<TIn>::load8(rowp + 32 * q + 8 * kg, hv);
+    __device__ __forceinline__ void store(u4 *Wl) const
+    {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const f4 wc = wop(Wl, q, 2, half, lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc = mfma(hv[4 * half + e], wc[e], acc);
+        for (int i = 0; i < kPer; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            if (idx < kEntries) {
+                const int ln = idx & 63;
+                const int rest = idx >> 6;
+                const Split s = split8(v[i]);
+                Wl[(rest * 2 + 0) * kWave + ln] = s.hi;
+                Wl[(rest * 2 + 1) * kWave + ln] = s.lo;
+            }
         }
     }
-    return acc;
+};
+
+__device__ __forceinline__ Split wop(const u4 *Wl, int q, int w, int lane)
+{
+    Split s;
+    s.hi = Wl[((q * 3 + w) * 2 + 0) * kWave + lane];
+    s.lo = Wl[((q * 3 + w) * 2 + 1) * kWave + lane];
+    return s;
 }
+
+// A|Bv projection of NB 16-row blocks (results in MFMA output layout).
+template <typename TIn, int NQ, int NB>
+__device__ __forceinline__ void project(const PBlk<TIn, NQ> (&blk)[NB], const u4 *Wl, int lane,
+                                        f4 (&aA)[NB], f4 (&aB)[NB])
+{
+    constexpr bool LO = PBlk<TIn, NQ>::kLo;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        aA[b] = zero4();
+        aB[b] = zero4();
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const Split wa = wop(Wl, q, 0, lane);
+        const Split wb = wop(Wl, q, 1, lane);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const Split h = blk[b].op(q);
+            aA[b] = mfma3<LO>(h, wa, aA[b]);
+            aB[b] = mfma3<LO>(h, wb, aB[b]);
+        }
+        // keep the weight-operand reads of later units from being hoisted here
+        // (they would pin NQ x 16 registers next to the in-flight rows)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// C projection partial over units q = wave + 4u for the group's 16 samples.
+template <typename TIn, int NQ>
+struct CvLoad {
+    static constexpr int kU = (NQ + kWaves - 1) / kWaves;
+    PBlk<TIn, 1> u[kU];
+    __device__ __forceinline__ void load(const TIn *__restrict__ row, int wave, int kg)
+    {
+#pragma unroll
+        for (int i = 0; i < kU; ++i) {
+            const int q = wave + kWaves * i;
+            if (q < NQ) u[i].load(row + 32 * q, kg);
+        }
+    }
+    __device__ __forceinline__ f4 partial(const u4 *Wl, int wave, int lane) const
+    {
+        constexpr bool LO = PBlk<TIn, 1>::kLo;
+        f4 acc = zero4();
+#pragma unroll
+        for (int i = 0; i < kU; ++i) {
+            const int q = wave + kWaves * i;
+            if (q < NQ) acc = mfma3<LO>(u[i].op(0), wop(Wl, q, 2, lane), acc);
+        }
+        return acc;
+    }
+};
 
 __device__ __forceinline__ void decode_block(int slices, int64_t &g, int &slice)
 {
@@ -257,16 +415,64 @@ __device__ __forceinline__ void decode_block(int slices, int64_t &g, int &slice)
 
 // ============================================================== forward kernel
 // Each wavefront owns four samples of the group and walks their rows in
-// 16-row blocks, carrying the state across blocks.
+// blocks of 16, carrying the state across blocks.  Two register buffers:
+// the loads of block b+1 are issued just before block b is projected, so
+// the memory system sees requests roughly in the order they are needed.
 template <typename TIn, int NQ>
-__global__ void __launch_bounds__(kThreads)
+__device__ __forceinline__ void fwd_block(const PBlk<TIn, NQ> &blk, const u4 *Wl, int base,
+                                          int lr_end, int K, int D, int s0, int64_t b0,
+                                          float a_shift, const float (*cvp)[16][16], int lane,
+                                          const LaneOff &lo, float &xc, float *__restrict__ ctx)
+{
+    const int kg = lane >> 4, ln = lane & 15;
+    const RowPos bp = base_pos(base, K);
+    f4 aA[1], aB[1];
+    {
+        const PBlk<TIn, NQ> one[1] = {blk};
+        project<TIn, NQ, 1>(one, Wl, lane, aA, aB);
+    }
+    Aff map[4];
+    Aff F = aff_id();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = base + 4 * kg + j;
+        Aff m;
+        if (r >= lr_end) {
+            m = aff_id();
+        } else {
+            m.m = sigmoid(aA[0][j] + a_shift);
+            m.c = aB[0][j];
+            m.r = row_pos(bp, lo, j, K).t == 0;
+        }
+        map[j] = m;
+        F = compose(m, F);
+    }
+    Aff excl, total;
+    scan_up(F, lane, excl, total);
+    float x = apply(excl, xc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        x = apply(map[j], x);
+        const int r = base + 4 * kg + j;
+        const RowPos rp = row_pos(bp, lo, j, K);
+        if (r < lr_end && rp.t == K - 1) {
+            const int bl = rp.bl;
+            const float cv = cvp[0][bl][ln] + cvp[1][bl][ln] + cvp[2][bl][ln] + cvp[3][bl][ln];
+            ctx[(b0 + bl) * D + s0 + ln] = cv * x;
+        }
+    }
+    xc = apply(total, xc);
+}
+
+template <typename TIn, int NQ>
+__global__ void __launch_bounds__(kThreads, NQ <= 8 ? 2 : 1)
 gscan_fwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                  const float *__restrict__ WA, const float *__restrict__ WB,
                  const float *__restrict__ WC, int64_t B, int K, int D, int slices,
                  int64_t groups, float a_shift, float *__restrict__ ctx)
 {
     constexpr int SH2 = NQ * 32;
-    __shared__ f4 Wl[NQ * 6 * kWave];
+    __shared__ u4 Wl[NQ * 6 * kWave];
     __shared__ float cvp[kWaves][16][16];
 
     int64_t g;
@@ -274,129 +480,157 @@ gscan_fwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     decode_block(slices, g, slice);
     if (g >= groups) return;
     const int s0 = slice * kSlice;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int kg = lane >> 4, ln = lane & 15;
-
-    stage_weights<NQ>(Wl, WA, WB, WC, D, s0);
-    __syncthreads();
-
     const int64_t b0 = g * kGroupSamples;
     const int nb = (int)(B - b0 < kGroupSamples ? B - b0 : kGroupSamples);
+    const int lr_begin = 4 * wave * K;
+    const int lr_end = (4 * wave + 4 < nb ? 4 * wave + 4 : nb) * K;
+    const bool active = lr_begin < lr_end;
+    const TIn *__restrict__ hg = hh + b0 * K * SH2;  // the group's first row
+    const LaneOff lo = lane_offsets(kg, K);
+    auto rowp = [&](int base) {
+        const int r = base + ln;
+        return hg + (uint32_t)((r < lr_end ? r : lr_end - 1) * SH2);
+    };
+
+    // loads in the order they are consumed: weights, h_s2, first h block
+    WStage<NQ> wst;
+    wst.load(WA, WB, WC, D, s0);
+    CvLoad<TIn, NQ> cvl;
+    cvl.load(hs2 + b0 * SH2 + (uint32_t)((ln < nb ? ln : nb - 1) * SH2), wave, kg);
+    PBlk<TIn, NQ> b0buf, b1buf;
+    if (active) b0buf.load(rowp(lr_begin), kg);
+    wst.store(Wl);
+    __syncthreads();
     {
-        const int sl = ln < nb ? ln : nb - 1;
-        const f4 cp = project_c_partial<TIn, NQ>(hs2 + (b0 + sl) * SH2, Wl, lane, wave);
+        const f4 cp = cvl.partial(Wl, wave, lane);
 #pragma unroll
         for (int j = 0; j < 4; ++j) cvp[wave][4 * kg + j][ln] = cp[j];
     }
     __syncthreads();
+    if (!active) return;
 
-    const int lr_begin = 4 * wave * K;
-    const int lr_end = (4 * wave + 4 < nb ? 4 * wave + 4 : nb) * K;
-    if (lr_begin >= lr_end) return;
-    const int64_t R0 = b0 * K;
     float xc = 0.f;
-    for (int lr0 = lr_begin; lr0 < lr_end; lr0 += kBlockRows) {
-        const int myr = lr0 + ln < lr_end ? lr0 + ln : lr_end - 1;
-        f4 aA, aB;
-        project_block<TIn, NQ>(hh + (R0 + myr) * SH2, Wl, lane, aA, aB);
-
-        Aff map[4];
-        Aff F = aff_id();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = lr0 + 4 * kg + j;
-            const int t = r % K;
-            Aff m;
-            if (r >= lr_end) {
-                m = aff_id();
-            } else {
-                m.m = sigmoid(aA[j] + a_shift);
-                m.c = aB[j];
-                m.r = t == 0;
-            }
-            map[j] = m;
-            F = compose(m, F);
-        }
-        Aff excl, total;
-        scan_up(F, lane, excl, total);
-        float x = apply(excl, xc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x = apply(map[j], x);
-            const int r = lr0 + 4 * kg + j;
-            if (r < lr_end && r % K == K - 1) {
-                const int bl = r / K;
-                const float cv = cvp[0][bl][ln] + cvp[1][bl][ln] + cvp[2][bl][ln] + cvp[3][bl][ln];
-                ctx[(b0 + bl) * D + s0 + ln] = cv * x;
-            }
-        }
-        xc = apply(total, xc);
+    for (int base = lr_begin; base < lr_end; base += 2 * kBlockRows) {
+        const int base1 = base + kBlockRows;
+        if (base1 < lr_end) b1buf.load(rowp(base1), kg);
+        fwd_block<TIn, NQ>(b0buf, Wl, base, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo, xc, ctx);
+        if (base1 >= lr_end) break;
+        if (base1 + kBlockRows < lr_end) b0buf.load(rowp(base1 + kBlockRows), kg);
+        fwd_block<TIn, NQ>(b1buf, Wl, base1, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo, xc, ctx);
     }
 }
 
 // ============================================================= backward kernel
-// Persistent over groups.  Rows of a group are processed in 64-row chunks,
-// wavefront w projecting block w of the chunk.  After the forward and
-// reverse scans (wavefronts combined through LDS), dL/dA and dL/dBv of the
-// chunk go to LDS and every wavefront contracts all 64 rows against its own
-// 64-column superblocks of SH2 (the "i split"), so each wavefront keeps only
-// SH2/8 gradient accumulators.
-//
-// A sample that continues past the chunk end (K not dividing the chunk)
-// needs the gates of later chunks.  Its rows' adjoints are computed with the
-// future gates set to 1 and summed into an "open" accumulator; when the next
-// chunk's gates of that sample are known the open accumulator is scaled by
-// their product (per state) and the new rows are added (Horner's scheme),
-// and once the sample ends the open accumulator is folded into the closed one.
-// 64-column superblocks of SH2, and how many of them one wavefront owns
 constexpr int nsb_of(int nq) { return nq * 32 / 64; }
 constexpr int sbw_of(int nq) { return (nsb_of(nq) + kWaves - 1) / kWaves; }
 
-// acc{A,B}[sbi][c] += sum over chunk rows r in [lo, hi) of h[r, i] (x) d{A,B}[r, s]
-// for i = 64*ib + 4*(4*(l/16) + jj) + c  (ib = wave + 4*sbi), s = l%16.
+// Rows of a chunk in the transposed ("T") layout for one 64-column
+// superblock ib: lane l holds columns 64*ib + 4*(l%16) + 0..3 of chunk row
+// 16(2*kap + e/4) + 4(l/16) + e%4 in hv[kap][e]; this row order is the
+// contraction's MFMA k index 8(l/16) + e.
 template <typename TIn, int NQ>
-__device__ __forceinline__ void contract_rows(
-    f4 (&accA)[sbw_of(NQ)][4], f4 (&accB)[sbw_of(NQ)][4],
-    const TIn *__restrict__ hh, int64_t R0, int cb, int NR, int lo, int hi,
-    const f4 (*dab)[2][kWave], int wave, int lane)
+__device__ __forceinline__ void load_t_half(f4 (&hv)[8], const TIn *__restrict__ hg, int cb,
+                                            int NR, int ib, int kap, int lane)
 {
     constexpr int SH2 = NQ * 32;
-    constexpr int NSB = nsb_of(NQ);
-    constexpr int SBW = sbw_of(NQ);
     const int kg = lane >> 4, ln = lane & 15;
 #pragma unroll
-    for (int sbi = 0; sbi < SBW; ++sbi) {
-        const int ib = wave + kWaves * sbi;
-        if (ib >= NSB) break;
+    for (int e = 0; e < 8; ++e) {
+        const int r = cb + kBlockRows * (2 * kap + e / 4) + 4 * kg + (e & 3);
+        const int rc = r < NR ? r : NR - 1;
+        hv[e] = Col4<TIn>::load(hg + (uint32_t)(rc * SH2 + 64 * ib + 4 * ln));
+    }
+}
+
+// acc{A,B}[c] += sum over the 32 chunk rows of half kap of h[r, i] (x) d{A,B}[r, s]
+// for i = 64*ib + 4*(4*(l/16) + jj) + c, s = l%16 (one superblock).
+template <bool LO>
+__device__ __forceinline__ void contract_half(f4 (&accA)[4], f4 (&accB)[4], const f4 (&hv)[8],
+                                              const Split &sA, const Split &sB)
+{
 #pragma unroll
-        for (int wb = 0; wb < kWaves; ++wb) {
-            const f4 dA4 = dab[wb][0][lane];
-            const f4 dB4 = dab[wb][1][lane];
-            f4 hv[4];
+    for (int c = 0; c < 4; ++c) {
+        float col[8];
 #pragma unroll
-            for (int jp = 0; jp < 4; ++jp) {
-                const int r = cb + kBlockRows * wb + 4 * kg + jp;
-                const int rc = r < NR ? r : NR - 1;
-                hv[jp] = In<TIn>::load4(hh + (R0 + rc) * SH2 + 64 * ib + 4 * ln);
-            }
+        for (int e = 0; e < 8; ++e) col[e] = hv[e][c];
+        const Split sh = split8(col);
+        accA[c] = mfma3<LO>(sh, sA, accA[c]);
+        accB[c] = mfma3<LO>(sh, sB, accB[c]);
+    }
+}
+
+// dL/dA, dL/dBv of chunk half kap as split B operands, rows outside [lo, hi) zeroed.
+__device__ __forceinline__ void grad_operands(Split &sA, Split &sB, const f4 (*dab)[2][kWave],
+                                              int kap, int cb, int lo, int hi, int lane)
+{
+    const int kg = lane >> 4;
+    const f4 a0 = dab[2 * kap][0][lane], a1 = dab[2 * kap + 1][0][lane];
+    const f4 b0 = dab[2 * kap][1][lane], b1 = dab[2 * kap + 1][1][lane];
+    float da[8], db[8];
 #pragma unroll
-            for (int jp = 0; jp < 4; ++jp) {
-                const int r = cb + kBlockRows * wb + 4 * kg + jp;
-                const bool in = r >= lo && r < hi;
-                const float da = in ? dA4[jp] : 0.f;
-                const float db = in ? dB4[jp] : 0.f;
+    for (int e = 0; e < 8; ++e) {
+        const int r = cb + kBlockRows * (2 * kap + e / 4) + 4 * kg + (e & 3);
+        const bool in = r >= lo && r < hi;
+        da[e] = in ? (e < 4 ? a0[e] : a1[e - 4]) : 0.f;
+        db[e] = in ? (e < 4 ? b0[e] : b1[e - 4]) : 0.f;
+    }
+    sA = split8(da);
+    sB = split8(db);
+}
+
+// All superblocks of this wavefront; hv0 holds superblock 0's rows when
+// EARLY (requested together with the chunk's projection rows, so they are
+// served from the same cache lines), otherwise rows are loaded here.
+template <typename TIn, int NQ, bool EARLY>
+__device__ __forceinline__ void contract_rows(f4 (&accA)[sbw_of(NQ)][4],
+                                              f4 (&accB)[sbw_of(NQ)][4], const f4 (&hv0)[2][8],
+                                              const TIn *__restrict__ hg, int cb, int NR, int lo,
+                                              int hi, const f4 (*dab)[2][kWave], int wave,
+                                              int lane)
+{
+    constexpr int NSB = nsb_of(NQ);
+    constexpr int SBW = sbw_of(NQ);
+    constexpr bool LO = PBlk<TIn, 1>::kLo;
+    if (wave >= NSB) return;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    accA[sbi][c] = mfma(hv[jp][c], da, accA[sbi][c]);
-                    accB[sbi][c] = mfma(hv[jp][c], db, accB[sbi][c]);
-                }
+    for (int kap = 0; kap < 2; ++kap) {
+        Split sA, sB;
+        grad_operands(sA, sB, dab, kap, cb, lo, hi, lane);
+#pragma unroll
+        for (int sbi = 0; sbi < SBW; ++sbi) {
+            const int ib = wave + kWaves * sbi;
+            if (ib >= NSB) break;
+            if (EARLY && sbi == 0) {
+                contract_half<LO>(accA[0], accB[0], hv0[kap], sA, sB);
+            } else {
+                f4 hv[8];
+                load_t_half<TIn, NQ>(hv, hg, cb, NR, ib, kap, lane);
+                contract_half<LO>(accA[sbi], accB[sbi], hv, sA, sB);
             }
         }
     }
 }
 
-template <typename TIn, int NQ>
-__global__ void __launch_bounds__(kThreads)
+// Persistent over groups.  Rows of a group are processed in 64-row chunks,
+// wavefront w projecting block w of the chunk.  dL/dA and dL/dBv of the
+// chunk go to LDS and every wavefront contracts all 64 rows against its own
+// 64-column superblocks of SH2 (the "i split"), so each wavefront keeps only
+// SH2/8 gradient accumulators per set.  The next chunk's rows (possibly the
+// next group's) are requested right after the current chunk's projection.
+//
+// ALIGNED (K divides 16): every 16-row block holds whole samples, so blocks
+// need no state from one another and the cross-wavefront scan is skipped.
+// Otherwise the forward state and the reverse adjoint are carried across
+// blocks through LDS, and a sample that continues past the chunk end is
+// handled with an "open" accumulator: its rows' adjoints are computed with
+// the future gates set to 1; when the next chunk's gates of that sample are
+// known the open accumulator is scaled by their product (per state) before
+// the new rows are added (Horner's scheme), and once the sample ends it is
+// folded into the closed accumulator.
+template <typename TIn, int NQ, bool ALIGNED>
+__global__ void __launch_bounds__(kThreads, NQ <= 8 ? 2 : 1)
 gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                  const float *__restrict__ WA, const float *__restrict__ WB,
                  const float *__restrict__ WC, int64_t B, int K, int D, int slices,
@@ -406,13 +640,14 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     constexpr int SH2 = NQ * 32;
     constexpr int NSB = nsb_of(NQ);
     constexpr int SBW = sbw_of(NQ);
-    __shared__ f4 Wl[NQ * 6 * kWave];
-    __shared__ float cvp[kWaves][16][16];
-    __shared__ float lamK[16][16];   // d_context * C  (dL/dx_K)
-    __shared__ float dctl[16][16];   // d_context slice
-    __shared__ float dCl[16][16];    // dL/dC = d_context * x_K
-    __shared__ float fsum[2][kWaves][3][16];
-    __shared__ float rsum[2][kWaves][3][16];
+    constexpr bool EARLY = SBW == 1;  // T rows requested with the chunk's projection rows
+    constexpr int NOPEN = ALIGNED ? 1 : SBW;  // open accumulators (unused when aligned)
+    __shared__ u4 Wl[NQ * 6 * kWave];
+    __shared__ float cvp[2][kWaves][16][16];  // C partials, by group parity
+    __shared__ float dctl[2][16][16];         // d_context slice, by group parity
+    __shared__ float dCl[2][16][16];          // dL/dC = d_context * x_K, by group parity
+    __shared__ float fsum[ALIGNED ? 1 : 2][kWaves][3][16];
+    __shared__ float rsum[ALIGNED ? 1 : 2][kWaves][3][16];
     __shared__ f4 dab[2][kWaves][2][kWave];
     __shared__ float gprev[2][16];
 
@@ -421,76 +656,124 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     decode_block(slices, rho, slice);
     const int s0 = slice * kSlice;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = wave_id();
     const int kg = lane >> 4, ln = lane & 15;
+    // (sample, step) of a row: shifts when K is a power of two dividing 16,
+    // otherwise the division-free offsets
+    const int kshift = __builtin_ctz((unsigned)K);
+    LaneOff lof;
+    if constexpr (!ALIGNED) lof = lane_offsets(kg, K);
+    auto rowpos = [&](const RowPos &bp, int lr, int j) {
+        if constexpr (ALIGNED) {
+            RowPos p = {lr >> kshift, lr & (K - 1)};
+            return p;
+        } else {
+            return row_pos(bp, lof, j, K);
+        }
+    };
 
-    f4 accAc[SBW][4], accAo[SBW][4], accBc[SBW][4], accBo[SBW][4], accC[SBW][4];
+    f4 accAc[SBW][4], accBc[SBW][4], accC[SBW][4];
+    f4 accAo[NOPEN][4], accBo[NOPEN][4];
 #pragma unroll
     for (int i = 0; i < SBW; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             accAc[i][c] = zero4();
-            accAo[i][c] = zero4();
             accBc[i][c] = zero4();
-            accBo[i][c] = zero4();
             accC[i][c] = zero4();
         }
+#pragma unroll
+    for (int i = 0; i < NOPEN; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            accAo[i][c] = zero4();
+            accBo[i][c] = zero4();
+        }
 
-    stage_weights<NQ>(Wl, WA, WB, WC, D, s0);
+    // rows of chunk c of group g for this wavefront's projection
+    auto prow = [&](int64_t gg, int cbase) {
+        const int64_t bb = gg * kGroupSamples;
+        const int nbb = (int)(B - bb < kGroupSamples ? B - bb : kGroupSamples);
+        const int nr = nbb * K;
+        const int r = cbase + kBlockRows * wave + ln;
+        return hh + bb * K * SH2 + (uint32_t)((r < nr ? r : nr - 1) * SH2);
+    };
 
-    for (int64_t g = rho; g < groups; g += nrows) {
-        __syncthreads();  // weights staged / previous group's LDS reads done
+    PBlk<TIn, NQ> pb;
+    {
+        WStage<NQ> wst;
+        wst.load(WA, WB, WC, D, s0);
+        wst.store(Wl);
+    }
+
+    int chunk_id = 0;
+    int gpar = 0;
+    for (int64_t g = rho; g < groups; g += nrows, gpar ^= 1) {
         const int64_t b0 = g * kGroupSamples;
         const int nb = (int)(B - b0 < kGroupSamples ? B - b0 : kGroupSamples);
-        {
-            const int sl = ln < nb ? ln : nb - 1;
-            const f4 cp = project_c_partial<TIn, NQ>(hs2 + (b0 + sl) * SH2, Wl, lane, wave);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) cvp[wave][4 * kg + j][ln] = cp[j];
-        }
-        __syncthreads();
-        {
-            const int bl = tid >> 4, s = tid & 15;
-            const float cv = cvp[0][bl][s] + cvp[1][bl][s] + cvp[2][bl][s] + cvp[3][bl][s];
-            const float d = bl < nb ? dctx[(b0 + bl) * D + s0 + s] : 0.f;
-            dctl[bl][s] = d;
-            lamK[bl][s] = d * cv;
-        }
-        __syncthreads();
-
-        const int64_t R0 = b0 * K;
+        const TIn *__restrict__ hg = hh + b0 * K * SH2;  // the group's first row
         const int NR = nb * K;
         const int nch = (NR + kChunkRows - 1) / kChunkRows;
+        {
+            CvLoad<TIn, NQ> cvl;
+            cvl.load(hs2 + b0 * SH2 + (uint32_t)((ln < nb ? ln : nb - 1) * SH2), wave, kg);
+            const int bl = tid >> 4, s = tid & 15;
+            dctl[gpar][bl][s] = bl < nb ? dctx[(b0 + bl) * D + s0 + s] : 0.f;
+            if (g == rho) __syncthreads();  // weights staged
+            const f4 cp = cvl.partial(Wl, wave, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cvp[gpar][wave][4 * kg + j][ln] = cp[j];
+        }
+        __syncthreads();
+        // lambda_K = dL/dx_K = d_context * C for local sample bl, state l%16
+        auto lam = [&](int bl) {
+            return dctl[gpar][bl][ln] * (cvp[gpar][0][bl][ln] + cvp[gpar][1][bl][ln] +
+                                         cvp[gpar][2][bl][ln] + cvp[gpar][3][bl][ln]);
+        };
+
         float xc = 0.f;
-        for (int c = 0; c < nch; ++c) {
-            const int buf = c & 1;
+        for (int c = 0; c < nch; ++c, ++chunk_id) {
+            const int buf = chunk_id & 1;
             const int cb = c * kChunkRows;
             const int ce = cb + kChunkRows < NR ? cb + kChunkRows : NR;
             const int lr0 = cb + kBlockRows * wave;
-            const int myr = lr0 + ln < NR ? lr0 + ln : NR - 1;
-            f4 aA, aB;
-            project_block<TIn, NQ>(hh + (R0 + myr) * SH2, Wl, lane, aA, aB);
+            // the chunk's projection rows and, right behind them, its transposed rows
+            f4 aA[1], aB[1];
+            f4 hv0[2][8];
+            pb.load(prow(g, cb), kg);
+            if constexpr (EARLY) {
+                if (wave < NSB) {
+                    load_t_half<TIn, NQ>(hv0[0], hg, cb, NR, wave, 0, lane);
+                    load_t_half<TIn, NQ>(hv0[1], hg, cb, NR, wave, 1, lane);
+                }
+            }
+            {
+                const PBlk<TIn, NQ> one[1] = {pb};
+                project<TIn, NQ, 1>(one, Wl, lane, aA, aB);
+            }
 
             // per-row maps (forward state and reverse adjoint)
+            RowPos bp = {0, 0};
+            if constexpr (!ALIGNED) bp = base_pos(lr0, K);
             Aff fm[4], rm[4];
             float gate[4];
             Aff F = aff_id();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = lr0 + 4 * kg + j;
-                const int bl = r / K;
-                const int t = r - bl * K;
-                const float gt = sigmoid(aA[j] + a_shift);
+                const RowPos rp = rowpos(bp, r, j);
+                const int bl = rp.bl, t = rp.t;
+                const float gt = sigmoid(aA[0][j] + a_shift);
                 gate[j] = gt;
                 if (r >= ce) {
                     fm[j] = aff_id();
                     rm[j] = aff_id();
                 } else {
                     fm[j].m = gt;
-                    fm[j].c = aB[j];
+                    fm[j].c = aB[0][j];
                     fm[j].r = t == 0;
                     rm[j].m = gt;
-                    rm[j].c = (t == 0 && bl > 0) ? lamK[bl - 1][ln] : 0.f;
+                    rm[j].c = (t == 0 && bl > 0) ? lam(bl - 1) : 0.f;
                     rm[j].r = t == 0;
                 }
                 F = compose(fm[j], F);
@@ -501,47 +784,53 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             Aff Fx, Ft, Rx, Rt;
             scan_up(F, lane, Fx, Ft);
             scan_down(R, lane, Rx, Rt);
-            if (kg == 0) {
-                fsum[buf][wave][0][ln] = Ft.m;
-                fsum[buf][wave][1][ln] = Ft.c;
-                fsum[buf][wave][2][ln] = (float)Ft.r;
-                rsum[buf][wave][0][ln] = Rt.m;
-                rsum[buf][wave][1][ln] = Rt.c;
-                rsum[buf][wave][2][ln] = (float)Rt.r;
-            }
-            __syncthreads();
 
-            // carries across wavefronts
-            float xin = xc, xnext = xc, gpre = 1.f, gall = 1.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                Aff a;
-                a.m = fsum[buf][w][0][ln];
-                a.c = fsum[buf][w][1][ln];
-                a.r = fsum[buf][w][2][ln] != 0.f;
-                if (w < wave) {
-                    xin = apply(a, xin);
-                    gpre *= a.m;
+            float xin = 0.f, xnext = 0.f, gpre = 1.f, gall = 1.f, mu;
+            if constexpr (ALIGNED) {
+                // the block starts a sample and ends one: no carries needed
+                const int last = (lr0 + kBlockRows < ce ? lr0 + kBlockRows : ce) - 1;
+                mu = last >= lr0 ? lam(last >> kshift) : 0.f;
+            } else {
+                if (kg == 0) {
+                    fsum[buf][wave][0][ln] = Ft.m;
+                    fsum[buf][wave][1][ln] = Ft.c;
+                    fsum[buf][wave][2][ln] = (float)Ft.r;
+                    rsum[buf][wave][0][ln] = Rt.m;
+                    rsum[buf][wave][1][ln] = Rt.c;
+                    rsum[buf][wave][2][ln] = (float)Rt.r;
                 }
-                xnext = apply(a, xnext);
-                gall *= a.m;
-            }
-            const int bl_top = (ce - 1) / K;
-            float mu = lamK[bl_top][ln];
+                __syncthreads();
+                xin = xc;
+                xnext = xc;
 #pragma unroll
-            for (int w = kWaves - 1; w >= 0; --w) {
-                if (w > wave) {
+                for (int w = 0; w < kWaves; ++w) {
                     Aff a;
-                    a.m = rsum[buf][w][0][ln];
-                    a.c = rsum[buf][w][1][ln];
-                    a.r = rsum[buf][w][2][ln] != 0.f;
-                    mu = apply(a, mu);
+                    a.m = fsum[buf][w][0][ln];
+                    a.c = fsum[buf][w][1][ln];
+                    a.r = fsum[buf][w][2][ln] != 0.f;
+                    if (w < wave) {
+                        xin = apply(a, xin);
+                        gpre *= a.m;
+                    }
+                    xnext = apply(a, xnext);
+                    gall *= a.m;
+                }
+                mu = lam((ce - 1) / K);
+#pragma unroll
+                for (int w = kWaves - 1; w >= 0; --w) {
+                    if (w > wave) {
+                        Aff a;
+                        a.m = rsum[buf][w][0][ln];
+                        a.c = rsum[buf][w][1][ln];
+                        a.r = rsum[buf][w][2][ln] != 0.f;
+                        mu = apply(a, mu);
+                    }
                 }
             }
 
-            // the sample open at the chunk start (if any) and where it ends
-            const bool has_prev = (cb % K) != 0;
-            const int prev_end = (cb / K + 1) * K - 1;  // its last local row
+            // the sample open at the chunk start (if any) and its last row
+            const bool has_prev = !ALIGNED && (cb % K) != 0;
+            const int prev_end = (cb / K + 1) * K - 1;
 
             // forward walk: state before each row, dL/dC at sample ends,
             // gate product of the open sample
@@ -551,12 +840,12 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = lr0 + 4 * kg + j;
-                const int bl = r / K;
-                const int t = r - bl * K;
+                const RowPos rp = rowpos(bp, r, j);
+                const int bl = rp.bl, t = rp.t;
                 xbef[j] = t == 0 ? 0.f : x;
                 x = apply(fm[j], x);
                 grun *= fm[j].m;
-                if (r < ce && t == K - 1) dCl[bl][ln] = dctl[bl][ln] * x;
+                if (r < ce && t == K - 1) dCl[gpar][bl][ln] = dctl[gpar][bl][ln] * x;
                 if (has_prev && r == prev_end) gprev[buf][ln] = grun;
             }
             // reverse walk: adjoint of each row's output state
@@ -576,54 +865,67 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             __syncthreads();
 
             // weight-gradient contraction of the chunk
-            const bool top_open = (bl_top + 1) * K > ce;
-            const int rN = top_open ? bl_top * K : ce;  // rows >= rN continue past the chunk
-            if (!has_prev && !top_open) {
-                contract_rows<TIn, NQ>(accAc, accBc, hh, R0, cb, NR, cb, ce, dab[buf], wave, lane);
+            if constexpr (ALIGNED) {
+                contract_rows<TIn, NQ, EARLY>(accAc, accBc, hv0, hg, cb, NR, cb, ce, dab[buf], wave,
+                                              lane);
             } else {
-                if (has_prev) {
-                    const float gs = prev_end < ce ? gprev[buf][ln] : gall;
+                const int bl_top = (ce - 1) / K;
+                const bool top_open = (bl_top + 1) * K > ce;
+                const int rN = top_open ? bl_top * K : ce;  // rows >= rN continue past the chunk
+                if (!has_prev && !top_open) {
+                    contract_rows<TIn, NQ, EARLY>(accAc, accBc, hv0, hg, cb, NR, cb, ce, dab[buf],
+                                                  wave, lane);
+                } else {
+                    if (has_prev) {
+                        const float gs = prev_end < ce ? gprev[buf][ln] : gall;
 #pragma unroll
-                    for (int i = 0; i < SBW; ++i)
+                        for (int i = 0; i < NOPEN; ++i)
 #pragma unroll
-                        for (int cc = 0; cc < 4; ++cc) {
-                            accAo[i][cc] *= gs;
-                            accBo[i][cc] *= gs;
-                        }
+                            for (int cc = 0; cc < 4; ++cc) {
+                                accAo[i][cc] *= gs;
+                                accBo[i][cc] *= gs;
+                            }
+                    }
+                    if (rN > cb) {
+                        contract_rows<TIn, NQ, EARLY>(accAo, accBo, hv0, hg, cb, NR, cb, rN, dab[buf],
+                                                      wave, lane);
+#pragma unroll
+                        for (int i = 0; i < NOPEN; ++i)
+#pragma unroll
+                            for (int cc = 0; cc < 4; ++cc) {
+                                accAc[i][cc] += accAo[i][cc];
+                                accBc[i][cc] += accBo[i][cc];
+                                accAo[i][cc] = zero4();
+                                accBo[i][cc] = zero4();
+                            }
+                    }
+                    if (rN < ce)
+                        contract_rows<TIn, NQ, EARLY>(accAo, accBo, hv0, hg, cb, NR, rN, ce, dab[buf],
+                                                      wave, lane);
                 }
-                if (rN > cb) {
-                    contract_rows<TIn, NQ>(accAo, accBo, hh, R0, cb, NR, cb, rN, dab[buf], wave,
-                                           lane);
-#pragma unroll
-                    for (int i = 0; i < SBW; ++i)
-#pragma unroll
-                        for (int cc = 0; cc < 4; ++cc) {
-                            accAc[i][cc] += accAo[i][cc];
-                            accBc[i][cc] += accBo[i][cc];
-                            accAo[i][cc] = zero4();
-                            accBo[i][cc] = zero4();
-                        }
-                }
-                if (rN < ce)
-                    contract_rows<TIn, NQ>(accAo, accBo, hh, R0, cb, NR, rN, ce, dab[buf], wave,
-                                           lane);
+                xc = xnext;
             }
-            xc = xnext;
         }
 
-        // dW_C rows of this group: h_s2^T @ dL/dC (dCl complete after the last barrier)
+        // dW_C rows of this group: h_s2^T @ dL/dC (dCl complete after the last
+        // chunk's barrier), fp32 MFMA with k = 4 samples per step
 #pragma unroll
         for (int sbi = 0; sbi < SBW; ++sbi) {
             const int ib = wave + kWaves * sbi;
             if (ib >= NSB) break;
+            f4 hv[4];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int bl = 4 * a + kg;
                 const int blc = bl < nb ? bl : nb - 1;
-                const f4 hv = In<TIn>::load4(hs2 + (b0 + blc) * SH2 + 64 * ib + 4 * ln);
-                const float dc = bl < nb ? dCl[bl][ln] : 0.f;
+                hv[a] = Col4<TIn>::load(hs2 + b0 * SH2 + (uint32_t)(blc * SH2 + 64 * ib + 4 * ln));
+            }
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) accC[sbi][cc] = mfma(hv[cc], dc, accC[sbi][cc]);
+            for (int a = 0; a < 4; ++a) {
+                const int bl = 4 * a + kg;
+                const float dc = bl < nb ? dCl[gpar][bl][ln] : 0.f;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) accC[sbi][cc] = mfma_f32(hv[a][cc], dc, accC[sbi][cc]);
             }
         }
     }
@@ -648,25 +950,47 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 }
 
 // ================================================= phase 2: partial reduction
-// out[o] = sum over rho (fixed order: four interleaved lanes of partials,
-// then their sum) of part[rho][o], o over the 3*SH2*D gradient entries.
+// Workgroup = 64 consecutive gradient entries; thread (seg, quad) sums rows
+// r = seg, seg+16, ... of four consecutive entries; the 16 row segments are
+// then added in segment order.  Fixed order, so bitwise reproducible.
+constexpr int kRedCols = 64;
+constexpr int kRedSegs = kThreads / (kRedCols / 4);
+
 __global__ void __launch_bounds__(kThreads)
 gscan_reduce_kernel(const float *__restrict__ part, int64_t nrows, int64_t wsz,
                     float *__restrict__ dWA, float *__restrict__ dWB, float *__restrict__ dWC)
 {
-    __shared__ double red[4][64];
+    __shared__ double red[kRedSegs][kRedCols];
     const int t = threadIdx.x;
-    const int seg = t >> 6;
-    const int64_t o = (int64_t)blockIdx.x * 64 + (t & 63);
+    const int quad = t & 15, seg = t >> 4;
     const int64_t per = 3 * wsz;
-    double s = 0.0;
-    if (o < per)
-        for (int64_t r = seg; r < nrows; r += 4) s += (double)part[r * per + o];
-    red[seg][t & 63] = s;
+    const int64_t o = (int64_t)blockIdx.x * kRedCols + 4 * quad;
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+    const float *p = part + o;
+    int64_t r = seg;
+    for (; r + 3 * kRedSegs < nrows; r += 4 * kRedSegs) {
+        const f4 v0 = *reinterpret_cast<const f4 *>(p + r * per);
+        const f4 v1 = *reinterpret_cast<const f4 *>(p + (r + kRedSegs) * per);
+        const f4 v2 = *reinterpret_cast<const f4 *>(p + (r + 2 * kRedSegs) * per);
+        const f4 v3 = *reinterpret_cast<const f4 *>(p + (r + 3 * kRedSegs) * per);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[i] += ((double)v0[i] + (double)v1[i]) + ((double)v2[i] + (double)v3[i]);
+    }
+    for (; r < nrows; r += kRedSegs) {
+        const f4 v = *reinterpret_cast<const f4 *>(p + r * per);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] += (double)v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[seg][4 * quad + i] = s[i];
     __syncthreads();
-    if (seg == 0 && o < per) {
-        const double v = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
-        const int64_t which = o / wsz, e = o - which * wsz;
+    if (t < kRedCols) {
+        double v = 0.0;
+#pragma unroll
+        for (int sg = 0; sg < kRedSegs; ++sg) v += red[sg][t];
+        const int64_t oo = (int64_t)blockIdx.x * kRedCols + t;
+        const int64_t which = oo / wsz, e = oo - which * wsz;
         float *out = which == 0 ? dWA : (which == 1 ? dWB : dWC);
         out[e] = (float)v;
     }
@@ -689,10 +1013,17 @@ hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
                       const float *WB, const float *WC, float a_shift, const float *dctx,
                       float *part, hipStream_t st)
 {
-    hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ>), dim3((unsigned)p.bwd_grid), dim3(kThreads), 0,
-                       st, static_cast<const TIn *>(hh), static_cast<const TIn *>(hs2), WA, WB,
-                       WC, p.B, (int)p.K, (int)p.D, p.slices, p.groups, p.bwd_rows, a_shift,
-                       dctx, part);
+    const bool aligned = 16 % p.K == 0;
+    if (aligned)
+        hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ, true>), dim3((unsigned)p.bwd_grid),
+                           dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
+                           static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
+                           p.slices, p.groups, p.bwd_rows, a_shift, dctx, part);
+    else
+        hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ, false>), dim3((unsigned)p.bwd_grid),
+                           dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
+                           static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
+                           p.slices, p.groups, p.bwd_rows, a_shift, dctx, part);
     return hipGetLastError();
 }
 
@@ -738,8 +1069,8 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
     if (B < 1 || K < 1 || SH2 < 64 || SH2 > kMaxSH2 || SH2 % 64 != 0 || D < kSlice ||
         D > kMaxD || D % kSlice != 0 || (dtype != 0 && dtype != 1))
         return false;
-    // local row indices (16 samples x K) and global row counts stay in range
-    if (K > (int64_t(1) << 26) || B > (int64_t(1) << 40) || B * K > (int64_t(1) << 46))
+    // 32-bit element offsets inside a 16-sample group (16 * K * SH2 < 2^31)
+    if (K > (int64_t(1) << 18) || B > (int64_t(1) << 40) || B * K > (int64_t(1) << 46))
         return false;
     Plan q;
     q.B = B;
@@ -760,7 +1091,7 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
     q.bwd_rows = q.fwd_rows < cap ? q.fwd_rows : cap;
     q.bwd_grid = q.bwd_rows * q.slices;
     const int64_t wsz = SH2 * D;
-    q.red_grid = (3 * wsz + 63) / 64;
+    q.red_grid = 3 * wsz / kRedCols;
     q.ws_bytes = (size_t)(q.bwd_rows * 3 * wsz * 4);
     if (q.fwd_grid > 0x7fffffff || q.bwd_grid > 0x7fffffff) return false;
     *p = q;

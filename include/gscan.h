@@ -24,7 +24,7 @@
  * h_history and h_s2 are float32 (GSCAN_F32) or bfloat16 (GSCAN_BF16, raw
  * 16-bit storage).  Everything else is float32; all accumulation is float32.
  *
- * Supported shapes: B >= 1, K >= 1, 64 <= SH2 <= 512 with SH2 % 64 == 0,
+ * Supported shapes: B >= 1, 1 <= K <= 262144, 64 <= SH2 <= 512 with SH2 % 64 == 0,
  * 16 <= D <= 256 with D % 16 == 0, B*K*SH2 < 2^62.
  *
  * Pointers: every array pointer is DEVICE memory owned by the caller,

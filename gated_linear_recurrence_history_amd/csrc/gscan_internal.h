@@ -31,6 +31,7 @@ struct Plan {
     int64_t fwd_grid = 0;
     int64_t bwd_grid = 0;
     int64_t red_grid = 0;
+    bool bwd_rows_kernel = false;  // backward via the K-divides-16 kernel
     size_t ws_bytes = 0;    // weight-gradient partials: bwd_rows x 3 x SH2 x D floats
 };
 

@@ -156,15 +156,19 @@ template <int NQ> struct PBlk<uint16_t, NQ> {
     }
 };
 
-// four consecutive columns of one row as float (transposed "T" layout loads)
+// four consecutive columns of one row (transposed "T" layout loads), kept
+// as stored until used so that a load never waits at its issue point
 template <typename T> struct Col4;
 template <> struct Col4<float> {
-    static __device__ __forceinline__ f4 load(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+    using raw_t = f4;
+    static __device__ __forceinline__ raw_t raw(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+    static __device__ __forceinline__ f4 widen(const raw_t &r) { return r; }
 };
 template <> struct Col4<uint16_t> {
-    static __device__ __forceinline__ f4 load(const uint16_t *p)
+    using raw_t = uint2;
+    static __device__ __forceinline__ raw_t raw(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+    static __device__ __forceinline__ f4 widen(const raw_t &u)
     {
-        const uint2 u = *reinterpret_cast<const uint2 *>(p);
         f4 r;
         r[0] = bf_lo(u.x);
         r[1] = bf_hi(u.x);
@@ -301,45 +305,79 @@ __device__ __forceinline__ int wave_id()
 // LDS image of [W_A | W_B | W_C][:, s0 .. s0+16) as bf16 hi/lo in MFMA
 // B-operand order: entry ((q*3 + w)*2 + part)*64 + lane holds rows
 // 32q + 8(lane/16) + 0..7 of weight w for state s0 + lane%16.
-// Loaded into registers first (so the loads are in flight early), then
-// split and stored.
-template <int NQ>
+// The slice rows (16 contiguous floats each) are fetched with 16-byte loads,
+// all issued up front; the rearrangement goes through a raw LDS tile of
+// kRawRows rows, one weight (and row range) per round.
+// largest multiple of 64 rows that divides SH2 and fits 16 KiB (256 rows)
+constexpr int raw_rows_of(int nq)
+{
+    int best = 64;
+    for (int r = 64; r <= 256; r += 64)
+        if ((nq * 32) % r == 0) best = r;
+    return best;
+}
+
+template <int NQ, int NT = kThreads>
 struct WStage {
-    static constexpr int kEntries = NQ * 3 * kWave;
-    static constexpr int kPer = (kEntries + kThreads - 1) / kThreads;
-    float v[kPer][8];
+    static constexpr int SH2 = NQ * 32;
+    static constexpr int kRawRows = raw_rows_of(NQ);
+    static constexpr int kPieces = SH2 * 4;                  // 16-byte pieces per weight
+    static constexpr int kPer = (kPieces + NT - 1) / NT;     // per thread per weight
+    static constexpr int kRounds = SH2 / kRawRows;           // row ranges per weight
+    static_assert(SH2 % kRawRows == 0 && kRawRows % 64 == 0, "row ranges of whole pieces");
+    static_assert(kRounds == 1 || (kRawRows * 4) % NT == 0, "pieces of a round per thread");
+    f4 v[3][kPer];
 
     __device__ __forceinline__ void load(const float *__restrict__ WA, const float *__restrict__ WB,
                                          const float *__restrict__ WC, int D, int s0)
     {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int idx = threadIdx.x + i * kThreads;
-            if (idx < kEntries) {
-                const int ln = idx & 63;
-                const int rest = idx >> 6;
-                const int w = rest % 3;
-                const int q = rest / 3;
-                const float *W = w == 0 ? WA : (w == 1 ? WB : WC);
-                const float *p = W + (32 * q + 8 * (ln >> 4)) * D + s0 + (ln & 15);
+        for (int w = 0; w < 3; ++w) {
+            const float *W = w == 0 ? WA : (w == 1 ? WB : WC);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[i][e] = p[e * D];
+            for (int i = 0; i < kPer; ++i) {
+                // row idx/4, columns 4(idx%4)..; clamped rather than guarded so
+                // that no path skips a load (waits for older loads stay exact)
+                const int idx = kPieces % NT == 0 ? threadIdx.x + i * NT
+                                                  : min(threadIdx.x + i * NT, kPieces - 1);
+                v[w][i] = *reinterpret_cast<const f4 *>(W + (idx >> 2) * D + s0 + 4 * (idx & 3));
             }
         }
     }
-    __device__ __forceinline__ void store(u4 *Wl) const
+    // raw: kRawRows * 16 floats of LDS, free during the call.  Ends with the
+    // image written; the caller's barrier publishes it.
+    __device__ __forceinline__ void store(u4 *Wl, float *raw) const
     {
+        constexpr int kEntries = kRawRows / 32 * kWave;  // image entries per round
+        constexpr int kPerRound = kRounds == 1 ? kPer : kRawRows * 4 / NT;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int idx = threadIdx.x + i * kThreads;
-            if (idx < kEntries) {
-                const int ln = idx & 63;
-                const int rest = idx >> 6;
-                const Split s = split8(v[i]);
-                Wl[(rest * 2 + 0) * kWave + ln] = s.hi;
-                Wl[(rest * 2 + 1) * kWave + ln] = s.lo;
+        for (int w = 0; w < 3; ++w)
+#pragma unroll
+            for (int rc = 0; rc < kRounds; ++rc) {
+                if (w + rc > 0) __syncthreads();  // previous round's reads done
+#pragma unroll
+                for (int i = 0; i < kPerRound; ++i) {
+                    const int idx = threadIdx.x + i * NT;
+                    if (kRounds > 1 || kPieces % NT == 0 || idx < kPieces)
+                        *reinterpret_cast<f4 *>(raw + 4 * idx) = v[w][rc * kPerRound + i];
+                }
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < (kEntries + NT - 1) / NT; ++j) {
+                    const int e = threadIdx.x + j * NT;
+                    if (e < kEntries) {
+                        const int ql = e >> 6, ln = e & 63;
+                        float x[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            x[k] = raw[(32 * ql + 8 * (ln >> 4) + k) * 16 + (ln & 15)];
+                        const Split sp = split8(x);
+                        const int q = rc * (kRawRows / 32) + ql;
+                        Wl[((q * 3 + w) * 2 + 0) * kWave + ln] = sp.hi;
+                        Wl[((q * 3 + w) * 2 + 1) * kWave + ln] = sp.lo;
+                    }
+                }
             }
-        }
     }
 };
 
@@ -385,20 +423,25 @@ struct CvLoad {
     PBlk<TIn, 1> u[kU];
     __device__ __forceinline__ void load(const TIn *__restrict__ row, int wave, int kg)
     {
+        // every unit loaded (clamped) so that no path skips a load
 #pragma unroll
         for (int i = 0; i < kU; ++i) {
             const int q = wave + kWaves * i;
-            if (q < NQ) u[i].load(row + 32 * q, kg);
+            u[i].load(row + 32 * (q < NQ ? q : NQ - 1), kg);
         }
     }
     __device__ __forceinline__ f4 partial(const u4 *Wl, int wave, int lane) const
     {
+        // unconditional products (a unit past SH2 repeats the last one and is
+        // dropped by the select), so the loads have unconditional uses and
+        // stay where they were issued
         constexpr bool LO = PBlk<TIn, 1>::kLo;
         f4 acc = zero4();
 #pragma unroll
         for (int i = 0; i < kU; ++i) {
             const int q = wave + kWaves * i;
-            if (q < NQ) acc = mfma3<LO>(u[i].op(0), wop(Wl, q, 2, lane), acc);
+            const f4 t = mfma3<LO>(u[i].op(0), wop(Wl, q < NQ ? q : NQ - 1, 2, lane), acc);
+            acc = q < NQ ? t : acc;
         }
         return acc;
     }
@@ -474,6 +517,7 @@ gscan_fwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     constexpr int SH2 = NQ * 32;
     __shared__ u4 Wl[NQ * 6 * kWave];
     __shared__ float cvp[kWaves][16][16];
+    __shared__ f4 wraw[raw_rows_of(NQ) * 4];
 
     int64_t g;
     int slice;
@@ -500,8 +544,8 @@ gscan_fwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     CvLoad<TIn, NQ> cvl;
     cvl.load(hs2 + b0 * SH2 + (uint32_t)((ln < nb ? ln : nb - 1) * SH2), wave, kg);
     PBlk<TIn, NQ> b0buf, b1buf;
-    if (active) b0buf.load(rowp(lr_begin), kg);
-    wst.store(Wl);
+    b0buf.load(rowp(lr_begin), kg);  // clamped: a valid row even for an idle wavefront
+    wst.store(Wl, reinterpret_cast<float *>(wraw));
     __syncthreads();
     {
         const f4 cp = cvl.partial(Wl, wave, lane);
@@ -511,13 +555,15 @@ gscan_fwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     __syncthreads();
     if (!active) return;
 
+    // the next block is always requested (clamped to the last row past the
+    // end), so the wait for the current block leaves it in flight
     float xc = 0.f;
     for (int base = lr_begin; base < lr_end; base += 2 * kBlockRows) {
         const int base1 = base + kBlockRows;
-        if (base1 < lr_end) b1buf.load(rowp(base1), kg);
+        b1buf.load(rowp(base1), kg);
         fwd_block<TIn, NQ>(b0buf, Wl, base, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo, xc, ctx);
         if (base1 >= lr_end) break;
-        if (base1 + kBlockRows < lr_end) b0buf.load(rowp(base1 + kBlockRows), kg);
+        b0buf.load(rowp(base1 + kBlockRows), kg);
         fwd_block<TIn, NQ>(b1buf, Wl, base1, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo, xc, ctx);
     }
 }
@@ -528,11 +574,12 @@ constexpr int sbw_of(int nq) { return (nsb_of(nq) + kWaves - 1) / kWaves; }
 
 // Rows of a chunk in the transposed ("T") layout for one 64-column
 // superblock ib: lane l holds columns 64*ib + 4*(l%16) + 0..3 of chunk row
-// 16(2*kap + e/4) + 4(l/16) + e%4 in hv[kap][e]; this row order is the
+// 16(2*kap + e/4) + 4(l/16) + e%4 in hv[e]; this row order is the
 // contraction's MFMA k index 8(l/16) + e.
 template <typename TIn, int NQ>
-__device__ __forceinline__ void load_t_half(f4 (&hv)[8], const TIn *__restrict__ hg, int cb,
-                                            int NR, int ib, int kap, int lane)
+__device__ __forceinline__ void load_t_half(typename Col4<TIn>::raw_t (&hv)[8],
+                                            const TIn *__restrict__ hg, int cb, int NR, int ib,
+                                            int kap, int lane)
 {
     constexpr int SH2 = NQ * 32;
     const int kg = lane >> 4, ln = lane & 15;
@@ -540,21 +587,26 @@ __device__ __forceinline__ void load_t_half(f4 (&hv)[8], const TIn *__restrict__
     for (int e = 0; e < 8; ++e) {
         const int r = cb + kBlockRows * (2 * kap + e / 4) + 4 * kg + (e & 3);
         const int rc = r < NR ? r : NR - 1;
-        hv[e] = Col4<TIn>::load(hg + (uint32_t)(rc * SH2 + 64 * ib + 4 * ln));
+        hv[e] = Col4<TIn>::raw(hg + (uint32_t)(rc * SH2 + 64 * ib + 4 * ln));
     }
 }
 
 // acc{A,B}[c] += sum over the 32 chunk rows of half kap of h[r, i] (x) d{A,B}[r, s]
 // for i = 64*ib + 4*(4*(l/16) + jj) + c, s = l%16 (one superblock).
-template <bool LO>
-__device__ __forceinline__ void contract_half(f4 (&accA)[4], f4 (&accB)[4], const f4 (&hv)[8],
+template <typename TIn>
+__device__ __forceinline__ void contract_half(f4 (&accA)[4], f4 (&accB)[4],
+                                              const typename Col4<TIn>::raw_t (&hv)[8],
                                               const Split &sA, const Split &sB)
 {
+    constexpr bool LO = PBlk<TIn, 1>::kLo;
+    f4 w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = Col4<TIn>::widen(hv[e]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         float col[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) col[e] = hv[e][c];
+        for (int e = 0; e < 8; ++e) col[e] = w[e][c];
         const Split sh = split8(col);
         accA[c] = mfma3<LO>(sh, sA, accA[c]);
         accB[c] = mfma3<LO>(sh, sB, accB[c]);
@@ -580,19 +632,19 @@ __device__ __forceinline__ void grad_operands(Split &sA, Split &sB, const f4 (*d
     sB = split8(db);
 }
 
-// All superblocks of this wavefront; hv0 holds superblock 0's rows when
+// All superblocks of this wavefront; hv0 holds superblock `wave`'s rows when
 // EARLY (requested together with the chunk's projection rows, so they are
 // served from the same cache lines), otherwise rows are loaded here.
 template <typename TIn, int NQ, bool EARLY>
 __device__ __forceinline__ void contract_rows(f4 (&accA)[sbw_of(NQ)][4],
-                                              f4 (&accB)[sbw_of(NQ)][4], const f4 (&hv0)[2][8],
+                                              f4 (&accB)[sbw_of(NQ)][4],
+                                              const typename Col4<TIn>::raw_t (&hv0)[2][8],
                                               const TIn *__restrict__ hg, int cb, int NR, int lo,
                                               int hi, const f4 (*dab)[2][kWave], int wave,
                                               int lane)
 {
     constexpr int NSB = nsb_of(NQ);
     constexpr int SBW = sbw_of(NQ);
-    constexpr bool LO = PBlk<TIn, 1>::kLo;
     if (wave >= NSB) return;
 #pragma unroll
     for (int kap = 0; kap < 2; ++kap) {
@@ -603,11 +655,11 @@ __device__ __forceinline__ void contract_rows(f4 (&accA)[sbw_of(NQ)][4],
             const int ib = wave + kWaves * sbi;
             if (ib >= NSB) break;
             if (EARLY && sbi == 0) {
-                contract_half<LO>(accA[0], accB[0], hv0[kap], sA, sB);
+                contract_half<TIn>(accA[0], accB[0], hv0[kap], sA, sB);
             } else {
-                f4 hv[8];
+                typename Col4<TIn>::raw_t hv[8];
                 load_t_half<TIn, NQ>(hv, hg, cb, NR, ib, kap, lane);
-                contract_half<LO>(accA[sbi], accB[sbi], hv, sA, sB);
+                contract_half<TIn>(accA[sbi], accB[sbi], hv, sA, sB);
             }
         }
     }
@@ -701,9 +753,11 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 
     PBlk<TIn, NQ> pb;
     {
+        // the adjoint buffer doubles as the raw tile of the weight staging
         WStage<NQ> wst;
         wst.load(WA, WB, WC, D, s0);
-        wst.store(Wl);
+        static_assert(sizeof(dab) >= raw_rows_of(NQ) * 16 * sizeof(float), "raw tile");
+        wst.store(Wl, reinterpret_cast<float *>(dab));
     }
 
     int chunk_id = 0;
@@ -739,7 +793,7 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             const int lr0 = cb + kBlockRows * wave;
             // the chunk's projection rows and, right behind them, its transposed rows
             f4 aA[1], aB[1];
-            f4 hv0[2][8];
+            typename Col4<TIn>::raw_t hv0[2][8];
             pb.load(prow(g, cb), kg);
             if constexpr (EARLY) {
                 if (wave < NSB) {
@@ -918,7 +972,8 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             for (int a = 0; a < 4; ++a) {
                 const int bl = 4 * a + kg;
                 const int blc = bl < nb ? bl : nb - 1;
-                hv[a] = Col4<TIn>::load(hs2 + b0 * SH2 + (uint32_t)(blc * SH2 + 64 * ib + 4 * ln));
+                hv[a] = Col4<TIn>::widen(
+                    Col4<TIn>::raw(hs2 + b0 * SH2 + (uint32_t)(blc * SH2 + 64 * ib + 4 * ln)));
             }
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -949,11 +1004,449 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     }
 }
 
+struct BTask {
+    int64_t g;  // group (no task when g >= groups)
+    int c;      // chunk within the group
+    int k;      // ordinal of the group in this workgroup (LDS parity)
+    int n;      // ordinal of the chunk in this workgroup
+};
+
+// ============================================ backward, K dividing 16 ("rows")
+// When K divides 16 every 16-row block holds whole samples, so a wavefront
+// can finish its block alone: projection replay, scans and adjoints as in
+// the kernel above, then the weight-gradient contraction over the block's
+// own 16 rows.  That contraction needs h with rows along the MFMA k index,
+// while the row loads put columns along k.  The split block (bf16 high and
+// low planes) goes to a per-wavefront LDS tile right after the split, and
+// ds_read_b64_tr_b16 reads it back transposed: four rows of one column per
+// lane.  Four rows of high parts and the same four rows of low parts make
+// one k = 32 operand [high | low]; its products with [dhigh | dhigh] and
+// [dlow | 0] give the three terms of the split product in two MFMAs.  No
+// transposed reloads, no second split, no LDS exchange between wavefronts.
+// Every wavefront accumulates all SH2 columns; the four sums are added
+// through LDS at the end in a fixed order.  One persistent workgroup per CU;
+// the next chunk's rows (and the next group's h_s2 rows) are requested
+// before the current chunk is computed.
+
+// B[k][n] = (k == 16t + n) in bf16; lane l holds k = 8(l/16) + e, n = l%16
+__device__ __forceinline__ u4 select_operand(int t, int lane)
+{
+    const int e = 16 * t + (lane & 15) - 8 * (lane >> 4);
+    u4 r;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        r[d] = (e == 2 * d ? 0x3f80u : 0u) | (e == 2 * d + 1 ? 0x3f800000u : 0u);
+    return r;
+}
+
+// columns 16t .. 16t+15 of a split 32-column unit as a contraction A operand:
+// lane l -> column 16t + l%16; k = 8(l/16) + e holds row 4(l/16) + e%4, high
+// part for e < 4 and low part for e >= 4 (high again when LO is false)
+template <bool LO>
+__device__ __forceinline__ u4 transpose_unit(const Split &s, const u4 &sel)
+{
+    const f4 th = mfma_bf(s.hi, sel, zero4());
+    u4 r;
+    r[0] = pack_bf16(th[0], th[1]);
+    r[1] = pack_bf16(th[2], th[3]);
+    if constexpr (LO) {
+        const f4 tl = mfma_bf(s.lo, sel, zero4());
+        r[2] = pack_bf16(tl[0], tl[1]);
+        r[3] = pack_bf16(tl[2], tl[3]);
+    } else {
+        r[2] = r[0];
+        r[3] = r[1];
+    }
+    return r;
+}
+
+typedef short s4v __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i%4 of the 8-byte chunks addressed by lanes 4j + i/4, j = 0..3.  With lane
+// p of group g addressing row 4g + p/4, columns c + 4(p%4) .. +3 of a
+// row-major bf16 tile, lane i gets column c + i of rows 4g .. 4g+3.
+__device__ __forceinline__ uint2 read_tr(const uint16_t *p)
+{
+    const s4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4v *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// B operands for four rows 4(l/16) + j of one state: [dhigh | dhigh] and
+// [dlow | 0] (LO), or [dhigh | dlow] when the A operand is [high | high]
+struct GradOp {
+    u4 b1, b2;
+};
+
+template <bool LO>
+__device__ __forceinline__ GradOp grad_op(const f4 &d)
+{
+    const uint32_t h01 = pack_bf16(d[0], d[1]), h23 = pack_bf16(d[2], d[3]);
+    const uint32_t l01 = pack_bf16(d[0] - bf_lo(h01), d[1] - bf_hi(h01));
+    const uint32_t l23 = pack_bf16(d[2] - bf_lo(h23), d[3] - bf_hi(h23));
+    GradOp g;
+    if constexpr (LO) {
+        g.b1 = u4{h01, h23, h01, h23};
+        g.b2 = u4{l01, l23, 0u, 0u};
+    } else {
+        g.b1 = u4{h01, h23, l01, l23};
+        g.b2 = zero_u4();
+    }
+    return g;
+}
+
+template <bool LO>
+__device__ __forceinline__ f4 contract_op(const u4 &a, const GradOp &g, f4 acc)
+{
+    acc = mfma_bf(a, g.b1, acc);
+    if constexpr (LO) acc = mfma_bf(a, g.b2, acc);
+    return acc;
+}
+
+// Workgroup of 8 wavefronts, two per SIMD: wavefronts w and w+4 share the
+// 16-row block w%4 of each 64-row chunk, each owning half of the SH2
+// columns (units h*NQ/2 .. (h+1)*NQ/2 - 1, h = w/4).  Each loads, splits and
+// projects its half; the two partial projections are added through LDS
+// (both wavefronts form the same sum, so both run identical scans); each
+// contracts its own half.  Gradient accumulators are then SH2/2 x 16 x 2 per
+// wavefront, which leaves room in 256 registers for the next chunk's rows.
+constexpr int kWaves2 = 8;
+constexpr int kThreads2 = kWave * kWaves2;
+
+template <typename TIn, int NQ>
+__global__ void __launch_bounds__(kThreads2, 1)
+gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
+                      const float *__restrict__ WA, const float *__restrict__ WB,
+                      const float *__restrict__ WC, int64_t B, int K, int D, int slices,
+                      int64_t groups, int64_t nrows, float a_shift,
+                      const float *__restrict__ dctx, float *__restrict__ part)
+{
+    constexpr int SH2 = NQ * 32;
+    constexpr int NH = NQ / 2;        // units per column half
+    constexpr int HC = SH2 / 2;       // columns per half
+    constexpr bool LO = PBlk<TIn, NQ>::kLo;
+    __shared__ u4 Wl[NQ * 6 * kWave];
+    __shared__ float cvp[kWaves2][16][16];  // C partials of the current group
+    __shared__ float dctl[16][16];          // d_context slice of the current group
+    __shared__ float dCl[16][16];           // dL/dC = d_context * x_K
+    __shared__ f4 xch[kWaves2][2][kWave];   // partial projections (A, B)
+    // per-wavefront transposition tile [plane hi|lo][row][column of the half],
+    // rows padded by 8 columns so the 16 rows of a transposed read spread
+    // over the banks; doubles as the raw tile of the weight staging and, at
+    // the end, as the cross-wavefront sums
+    constexpr int kPitch = HC + 8;
+    constexpr int kPlanes = LO ? 2 : 1;
+    constexpr int kStage = kWaves2 * kPlanes * 16 * kPitch * 2;
+    constexpr int kRed = 2 * 2 * SH2 * 16 * 4;
+    constexpr int kRaw = raw_rows_of(NQ) * 16 * 4;
+    constexpr int kMem = kStage > kRed ? (kStage > kRaw ? kStage : kRaw) : (kRed > kRaw ? kRed : kRaw);
+    __shared__ u4 stage_mem[kMem / 16];
+    // the current group's h_s2 unit `wave`, split: [wave][plane][sample][column]
+    __shared__ u4 hst_mem[kWaves2 * kPlanes * 16 * 32 * 2 / 16];
+
+    int64_t rho;
+    int slice;
+    decode_block(slices, rho, slice);
+    const int s0 = slice * kSlice;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = wave_id();
+    const int kg = lane >> 4, ln = lane & 15;
+    const int blk = wave & 3, half = wave >> 2;
+    const int kshift = __builtin_ctz((unsigned)K);  // K is a power of two <= 16
+    uint16_t *const tile = reinterpret_cast<uint16_t *>(stage_mem) + wave * kPlanes * 16 * kPitch;
+    uint16_t *const hst = reinterpret_cast<uint16_t *>(hst_mem) + wave * kPlanes * 16 * 32;
+    float(*const red)[2][SH2][16] = reinterpret_cast<float(*)[2][SH2][16]>(stage_mem);
+
+    f4 accA[NQ], accB[NQ], accC[2];  // i-tiles of this half; dW_C unit `wave`
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        accA[i] = zero4();
+        accB[i] = zero4();
+    }
+    accC[0] = zero4();
+    accC[1] = zero4();
+
+    auto samples_of = [&](int64_t gg) {
+        return (int)(B - gg * kGroupSamples < kGroupSamples ? B - gg * kGroupSamples
+                                                            : kGroupSamples);
+    };
+    auto advance = [&](const BTask &t) {
+        BTask n = t;
+        n.n = t.n + 1;
+        const int nch = (samples_of(t.g) * K + kChunkRows - 1) / kChunkRows;
+        if (t.c + 1 < nch) {
+            n.c = t.c + 1;
+        } else {
+            n.g = t.g + nrows;
+            n.c = 0;
+            n.k = t.k + 1;
+        }
+        return n;
+    };
+    // this wavefront's half of the projection rows of a chunk (block blk)
+    auto load_chunk = [&](const BTask &t, PBlk<TIn, NH> &pb) {
+        const int nr = samples_of(t.g) * K;
+        const int r = t.c * kChunkRows + kBlockRows * blk + ln;
+        pb.load(hh + t.g * kGroupSamples * K * SH2 + (uint32_t)((r < nr ? r : nr - 1) * SH2 + HC * half), kg);
+    };
+    // a group's h_s2 unit `wave` (C projection, dW_C) and d_context slice.
+    // Loads here and in load_chunk are unconditional (clamped addresses) so
+    // that every path issues the same loads and the waits for older ones
+    // can leave the younger ones in flight.
+    PBlk<TIn, 1> gcv;
+    float gdc = 0.f;
+    auto load_group = [&](int64_t gg) {
+        // uniform 64-bit bases, 32-bit lane offsets
+        const int nbb = samples_of(gg);
+        const int64_t bb = gg * kGroupSamples;
+        const TIn *const hsg = hs2 + bb * SH2;
+        const float *const dcg = dctx + bb * D + s0;
+        gcv.load(hsg + (uint32_t)((ln < nbb ? ln : nbb - 1) * SH2 + 32 * (wave % NQ)), kg);
+        const int bl = (tid >> 4) & 15, s = tid & 15;
+        gdc = dcg[(uint32_t)((bl < nbb ? bl : nbb - 1) * D + s)];  // masked at use
+    };
+    // C partials and d_context of a group into LDS (weights staged; every
+    // reader of the previous group's values is past a barrier)
+    auto use_group = [&](int nbb) {
+        // an opaque zero keeps these lane addresses from being hoisted out of
+        // the loop (and spilled): they are cheaper to recompute
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        const int ltid = tid + z, llane = lane + z;
+        // both halves write the same values; samples past the batch get 0
+        dctl[(ltid >> 4) & 15][ltid & 15] = ((ltid >> 4) & 15) < nbb ? gdc : 0.f;
+        // unconditional split and product (see CvLoad::partial); the split
+        // unit waits in LDS for this group's dW_C
+        const Split hsS = gcv.op(0);
+        uint16_t *const hw = hst + (llane & 15) * 32 + 8 * (llane >> 4);
+        *reinterpret_cast<u4 *>(hw) = hsS.hi;
+        if constexpr (LO) *reinterpret_cast<u4 *>(hw + 16 * 32) = hsS.lo;
+        f4 cp = mfma3<LO>(hsS, wop(Wl, wave % NQ, 2, llane), zero4());
+        if (wave >= NQ) cp = zero4();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cvp[wave][4 * (llane >> 4) + j][llane & 15] = cp[j];
+    };
+
+    auto step = [&](const BTask &cur, PBlk<TIn, NH> &pb, const BTask &nxt,
+                    PBlk<TIn, NH> &pbn) __attribute__((always_inline)) {
+        const int nb = samples_of(cur.g);
+        const int NR = nb * K;
+        const int nch = (NR + kChunkRows - 1) / kChunkRows;
+        const int c = cur.c;
+        const bool more = nxt.g < groups;
+        // the next group's rows (consumed at this step's end when the next
+        // chunk starts a group) go out first, the next chunk's rows right
+        // after this chunk's projection, once its registers are free
+        if (more && nxt.c == 0) load_group(nxt.g);
+        __syncthreads();  // last step's exchange read; this group's C partials visible
+        // lambda_K = dL/dx_K = d_context * C for local sample bl, state l%16
+        auto lam = [&](int bl) {
+            float cs = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves2; ++w) cs += cvp[w][bl][ln];
+            return dctl[bl][ln] * cs;
+        };
+        const int cb = c * kChunkRows;
+        const int ce = cb + kChunkRows < NR ? cb + kChunkRows : NR;
+        const int lr0 = cb + kBlockRows * blk;
+
+        // split this half once: projection from registers, contraction
+        // transposed from the wavefront's LDS tile
+        f4 pA = zero4(), pB = zero4();
+#pragma unroll
+        for (int u = 0; u < NH; ++u) {
+            const Split sp = pb.op(u);
+            *reinterpret_cast<u4 *>(tile + ln * kPitch + 32 * u + 8 * kg) = sp.hi;
+            if constexpr (LO)
+                *reinterpret_cast<u4 *>(tile + (16 + ln) * kPitch + 32 * u + 8 * kg) = sp.lo;
+            const int q = half * NH + u;
+            pA = mfma3<LO>(sp, wop(Wl, q, 0, lane), pA);
+            pB = mfma3<LO>(sp, wop(Wl, q, 1, lane), pB);
+            // keep later units' operand reads from being hoisted here
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        load_chunk(more ? nxt : cur, pbn);  // this chunk again after the last
+        xch[wave][0][lane] = pA;
+        xch[wave][1][lane] = pB;
+        __syncthreads();
+        const f4 aA = pA + xch[wave ^ 4][0][lane];  // same sum in both halves
+        const f4 aB = pB + xch[wave ^ 4][1][lane];
+
+        // per-row maps; the block starts and ends samples, so no carries
+        Aff fm[4], rm[4];
+        float gate[4];
+        Aff F = aff_id();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = lr0 + 4 * kg + j;
+            const int bl = r >> kshift, t = r & (K - 1);
+            const float gt = sigmoid(aA[j] + a_shift);
+            gate[j] = gt;
+            if (r >= ce) {
+                fm[j] = aff_id();
+                rm[j] = aff_id();
+            } else {
+                fm[j].m = gt;
+                fm[j].c = aB[j];
+                fm[j].r = t == 0;
+                rm[j].m = gt;
+                rm[j].c = (t == 0 && bl > 0) ? lam(bl - 1) : 0.f;
+                rm[j].r = t == 0;
+            }
+            F = compose(fm[j], F);
+        }
+        Aff R = aff_id();
+#pragma unroll
+        for (int j = 3; j >= 0; --j) R = compose(rm[j], R);
+        Aff Fx, Ft, Rx, Rt;
+        scan_up(F, lane, Fx, Ft);
+        scan_down(R, lane, Rx, Rt);
+        const int last = (lr0 + kBlockRows < ce ? lr0 + kBlockRows : ce) - 1;
+        const float mu = last >= lr0 ? lam(last >> kshift) : 0.f;
+
+        // forward walk: state before each row, dL/dC at sample ends
+        float x = apply(Fx, 0.f);
+        float xbef[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = lr0 + 4 * kg + j;
+            const int bl = r >> kshift, t = r & (K - 1);
+            xbef[j] = t == 0 ? 0.f : x;
+            x = apply(fm[j], x);
+            if (half == 0 && r < ce && t == K - 1) dCl[bl][ln] = dctl[bl][ln] * x;
+        }
+        // reverse walk: adjoint of each row's output state
+        float m_in = apply(Rx, mu);
+        f4 dA4, dB4;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+            const int r = lr0 + 4 * kg + j;
+            const bool v = r < ce;
+            const float gt = gate[j];
+            dB4[j] = v ? m_in : 0.f;
+            dA4[j] = v ? m_in * xbef[j] * (gt * (1.f - gt)) : 0.f;
+            m_in = apply(rm[j], m_in);
+        }
+
+        // weight-gradient contraction of this half over the block's 16 rows
+        const GradOp gA = grad_op<LO>(dA4), gB = grad_op<LO>(dB4);
+        const uint16_t *const trp = tile + (4 * kg + (ln >> 2)) * kPitch + 4 * (ln & 3);
+#pragma unroll
+        for (int tl = 0; tl < NQ; ++tl) {
+            const uint2 h = read_tr(trp + 16 * tl);
+            u4 av;
+            if constexpr (LO) {
+                const uint2 l = read_tr(trp + 16 * kPitch + 16 * tl);
+                av = u4{h.x, h.y, l.x, l.y};
+            } else {
+                av = u4{h.x, h.y, h.x, h.y};
+            }
+            accA[tl] = contract_op<LO>(av, gA, accA[tl]);
+            accB[tl] = contract_op<LO>(av, gB, accB[tl]);
+            if (tl % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounded read-ahead
+        }
+
+        if (c == nch - 1) {
+            __syncthreads();  // dL/dC of the whole group written
+            // dW_C of unit `wave` over the group's samples (k = sample), the
+            // split unit read back transposed
+            f4 dc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int bl = 4 * kg + e;
+                dc[e] = bl < nb ? dCl[bl][ln] : 0.f;
+            }
+            const GradOp gC = grad_op<LO>(dc);
+            const uint16_t *const hsp = hst + (4 * kg + (ln >> 2)) * 32 + 4 * (ln & 3);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint2 h = read_tr(hsp + 16 * t);
+                u4 av;
+                if constexpr (LO) {
+                    const uint2 l = read_tr(hsp + 16 * 32 + 16 * t);
+                    av = u4{h.x, h.y, l.x, l.y};
+                } else {
+                    av = u4{h.x, h.y, h.x, h.y};
+                }
+                accC[t] = contract_op<LO>(av, gC, accC[t]);
+            }
+            // the next group's C partials and d_context: every reader of this
+            // group's values (in the walks) is past the barrier above; dCl is
+            // rewritten only after the next step's first barrier
+            if (more) use_group(samples_of(nxt.g));
+        }
+    };
+
+    PBlk<TIn, NH> pA, pB;
+    BTask cur = {rho, 0, 0, 0};
+    {
+        WStage<NQ, kThreads2> wst;
+        wst.load(WA, WB, WC, D, s0);
+        const BTask t0 = {cur.g < groups ? cur.g : groups - 1, 0, 0, 0};
+        load_group(t0.g);
+        load_chunk(t0, pA);
+        wst.store(Wl, reinterpret_cast<float *>(stage_mem));
+    }
+    __syncthreads();  // weights staged
+    if (cur.g < groups) use_group(samples_of(cur.g));
+    while (cur.g < groups) {
+        BTask nxt = advance(cur);
+        step(cur, pA, nxt, pB);
+        if (nxt.g >= groups) break;
+        cur = nxt;
+        nxt = advance(cur);
+        step(cur, pB, nxt, pA);
+        cur = nxt;
+    }
+
+    // sums over the four blocks of each half: (b0 + b2) + (b1 + b3), in LDS
+    // (over the transposition tiles, once every wavefront is done with its own)
+    __syncthreads();
+    auto put = [&](int r, bool add) {
+#pragma unroll
+        for (int tl = 0; tl < NQ; ++tl)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = HC * half + 16 * tl + 4 * kg + j;
+                float &ra = red[r][0][i][ln];
+                float &rb = red[r][1][i][ln];
+                ra = add ? ra + accA[tl][j] : accA[tl][j];
+                rb = add ? rb + accB[tl][j] : accB[tl][j];
+            }
+    };
+    if (blk < 2) put(blk, false);
+    __syncthreads();
+    if (blk >= 2) put(blk - 2, true);
+    __syncthreads();
+    // this workgroup's partial: part[rho][which][i][s]
+    float *P = part + rho * 3 * (int64_t)SH2 * D;
+    constexpr int kVec = 2 * SH2 * 16 / 4;  // f4 entries of [A|B][i][s]
+    for (int v = tid; v < kVec; v += kThreads2) {
+        const int which = v / (SH2 * 4);
+        const int rem = v - which * SH2 * 4;
+        const int i = rem >> 2, s4 = (rem & 3) * 4;
+        const f4 r0 = *reinterpret_cast<const f4 *>(&red[0][which][i][s4]);
+        const f4 r1 = *reinterpret_cast<const f4 *>(&red[1][which][i][s4]);
+        *reinterpret_cast<f4 *>(P + which * (int64_t)SH2 * D + (int64_t)i * D + s0 + s4) = r0 + r1;
+    }
+    if (wave < NQ) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = 32 * wave + 16 * t + 4 * kg + j;
+                P[2 * (int64_t)SH2 * D + (int64_t)col * D + s0 + ln] = accC[t][j];
+            }
+    }
+}
+
 // ================================================= phase 2: partial reduction
-// Workgroup = 64 consecutive gradient entries; thread (seg, quad) sums rows
-// r = seg, seg+16, ... of four consecutive entries; the 16 row segments are
-// then added in segment order.  Fixed order, so bitwise reproducible.
-constexpr int kRedCols = 64;
+// Workgroup = 32 consecutive gradient entries; thread (seg, quad) sums rows
+// r = seg, seg+32, ... of four consecutive entries, eight rows in flight at
+// a time; the 32 row segments are then added in segment order.  Fixed order,
+// so bitwise reproducible.
+constexpr int kRedCols = 32;
 constexpr int kRedSegs = kThreads / (kRedCols / 4);
 
 __global__ void __launch_bounds__(kThreads)
@@ -962,20 +1455,20 @@ gscan_reduce_kernel(const float *__restrict__ part, int64_t nrows, int64_t wsz,
 {
     __shared__ double red[kRedSegs][kRedCols];
     const int t = threadIdx.x;
-    const int quad = t & 15, seg = t >> 4;
+    const int quad = t % (kRedCols / 4), seg = t / (kRedCols / 4);
     const int64_t per = 3 * wsz;
     const int64_t o = (int64_t)blockIdx.x * kRedCols + 4 * quad;
     double s[4] = {0.0, 0.0, 0.0, 0.0};
     const float *p = part + o;
     int64_t r = seg;
-    for (; r + 3 * kRedSegs < nrows; r += 4 * kRedSegs) {
-        const f4 v0 = *reinterpret_cast<const f4 *>(p + r * per);
-        const f4 v1 = *reinterpret_cast<const f4 *>(p + (r + kRedSegs) * per);
-        const f4 v2 = *reinterpret_cast<const f4 *>(p + (r + 2 * kRedSegs) * per);
-        const f4 v3 = *reinterpret_cast<const f4 *>(p + (r + 3 * kRedSegs) * per);
+    for (; r + 7 * kRedSegs < nrows; r += 8 * kRedSegs) {
+        f4 v[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s[i] += ((double)v0[i] + (double)v1[i]) + ((double)v2[i] + (double)v3[i]);
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f4 *>(p + (r + u * kRedSegs) * per);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[i] += (double)v[u][i];
     }
     for (; r < nrows; r += kRedSegs) {
         const f4 v = *reinterpret_cast<const f4 *>(p + r * per);
@@ -1014,6 +1507,15 @@ hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
                       float *part, hipStream_t st)
 {
     const bool aligned = 16 % p.K == 0;
+    if constexpr (NQ <= 8) {
+        if (p.bwd_rows_kernel) {
+            hipLaunchKernelGGL((gscan_bwd_rows_kernel<TIn, NQ>), dim3((unsigned)p.bwd_grid),
+                               dim3(kThreads2), 0, st, static_cast<const TIn *>(hh),
+                               static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
+                               p.slices, p.groups, p.bwd_rows, a_shift, dctx, part);
+            return hipGetLastError();
+        }
+    }
     if (aligned)
         hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ, true>), dim3((unsigned)p.bwd_grid),
                            dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
@@ -1083,9 +1585,11 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
     q.groups = (B + kGroupSamples - 1) / kGroupSamples;
     q.fwd_rows = (q.groups + kXcds - 1) / kXcds * kXcds;
     q.fwd_grid = q.fwd_rows * q.slices;
-    // backward: about two resident workgroups per CU when the weight slice
-    // leaves room for two in LDS, one otherwise (256 CUs)
-    const int64_t target = q.nq <= 8 ? 512 : 256;
+    // backward: the rows kernel (K divides 16, SH2 <= 256) runs one persistent
+    // workgroup per CU; the general kernel about two per CU when the weight
+    // slice leaves room for two in LDS, one otherwise (256 CUs)
+    q.bwd_rows_kernel = 16 % K == 0 && q.nq <= 8;
+    const int64_t target = (q.bwd_rows_kernel || q.nq > 8) ? 256 : 512;
     int64_t cap = target / q.slices / kXcds * kXcds;
     if (cap < kXcds) cap = kXcds;
     q.bwd_rows = q.fwd_rows < cap ? q.fwd_rows : cap;

@@ -1130,6 +1130,7 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     __shared__ float cvp[kWaves2][16][16];  // C partials of the current group
     __shared__ float dctl[16][16];          // d_context slice of the current group
     __shared__ float dCl[16][16];           // dL/dC = d_context * x_K
+    __shared__ float laml[16][16];          // lambda_K = d_context * C
     __shared__ f4 xch[kWaves2][2][kWave];   // partial projections (A, B)
     // per-wavefront transposition tile [plane hi|lo][row][column of the half],
     // rows padded by 8 columns so the 16 rows of a transposed read spread
@@ -1240,13 +1241,19 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         // after this chunk's projection, once its registers are free
         if (more && nxt.c == 0) load_group(nxt.g);
         __syncthreads();  // last step's exchange read; this group's C partials visible
-        // lambda_K = dL/dx_K = d_context * C for local sample bl, state l%16
-        auto lam = [&](int bl) {
-            float cs = 0.f;
+        if (c == 0) {
+            // lambda_K = dL/dx_K = d_context * C of the group's samples
+            if (wave < 4) {
+                int z;
+                asm volatile("s_mov_b32 %0, 0" : "=s"(z));  // keep the addresses local
+                const int bl = (tid + z) >> 4, s = (tid + z) & 15;
+                float cs = 0.f;
 #pragma unroll
-            for (int w = 0; w < kWaves2; ++w) cs += cvp[w][bl][ln];
-            return dctl[bl][ln] * cs;
-        };
+                for (int w = 0; w < kWaves2; ++w) cs += cvp[w][bl][s];
+                laml[bl][s] = dctl[bl][s] * cs;
+            }
+            __syncthreads();
+        }
         const int cb = c * kChunkRows;
         const int ce = cb + kChunkRows < NR ? cb + kChunkRows : NR;
         const int lr0 = cb + kBlockRows * blk;
@@ -1273,51 +1280,74 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         const f4 aA = pA + xch[wave ^ 4][0][lane];  // same sum in both halves
         const f4 aB = pB + xch[wave ^ 4][1][lane];
 
-        // per-row maps; the block starts and ends samples, so no carries
-        Aff fm[4], rm[4];
-        float gate[4];
-        Aff F = aff_id();
+        // The block starts and ends samples (K divides 16), so the scans stay
+        // inside the block: a lane's four rows hold one sample's rows when
+        // K >= 4, whole samples when K < 4; a sample spans kgs = K/4 lane
+        // groups.  Rows past the group's end are identity steps with zero
+        // gradients.  Resets are selects, never multiplications, so a
+        // non-finite value stays inside its sample.
+        float gate[4], beta[4];
+        int tj[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = lr0 + 4 * kg + j;
-            const int bl = r >> kshift, t = r & (K - 1);
+            tj[j] = r & (K - 1);
+            const bool v = r < ce;
             const float gt = sigmoid(aA[j] + a_shift);
-            gate[j] = gt;
-            if (r >= ce) {
-                fm[j] = aff_id();
-                rm[j] = aff_id();
-            } else {
-                fm[j].m = gt;
-                fm[j].c = aB[j];
-                fm[j].r = t == 0;
-                rm[j].m = gt;
-                rm[j].c = (t == 0 && bl > 0) ? lam(bl - 1) : 0.f;
-                rm[j].r = t == 0;
-            }
-            F = compose(fm[j], F);
+            gate[j] = v ? gt : 1.f;
+            beta[j] = v ? aB[j] : 0.f;
         }
-        Aff R = aff_id();
-#pragma unroll
-        for (int j = 3; j >= 0; --j) R = compose(rm[j], R);
-        Aff Fx, Ft, Rx, Rt;
-        scan_up(F, lane, Fx, Ft);
-        scan_down(R, lane, Rx, Rt);
-        const int last = (lr0 + kBlockRows < ce ? lr0 + kBlockRows : ce) - 1;
-        const float mu = last >= lr0 ? lam(last >> kshift) : 0.f;
+        const int kgs = K >> 2;                       // lane groups per sample (K >= 8: 2 or 4)
+        const int sub = kgs > 1 ? (kg & (kgs - 1)) : 0;  // lane group within its sample
+        const float G = gate[0] * gate[1] * gate[2] * gate[3];
+        float x_in = 0.f, gsuf = 1.f;  // state entering the lane; gates of later groups
+        if (kgs > 1) {
+            // forward: affine map of the lane's rows, prefix over the sample's groups
+            float M = G, C = beta[0];
+            C = gate[1] * C + beta[1];
+            C = gate[2] * C + beta[2];
+            C = gate[3] * C + beta[3];
+            float pM = __shfl(M, lane >= 16 ? lane - 16 : lane);
+            float pC = __shfl(C, lane >= 16 ? lane - 16 : lane);
+            if (sub >= 1) {
+                C = M * pC + C;
+                M = M * pM;
+            }
+            if (kgs > 2) {
+                pM = __shfl(M, lane >= 32 ? lane - 32 : lane);
+                pC = __shfl(C, lane >= 32 ? lane - 32 : lane);
+                if (sub >= 2) {
+                    C = M * pC + C;
+                    M = M * pM;
+                }
+            }
+            const float e = __shfl(C, lane >= 16 ? lane - 16 : lane);
+            x_in = sub >= 1 ? e : 0.f;
+            // reverse: product of the gates of the sample's later groups
+            float S = G;
+            float q = __shfl(S, lane < 48 ? lane + 16 : lane);
+            if (sub <= kgs - 2) S *= q;
+            if (kgs > 2) {
+                q = __shfl(S, lane < 32 ? lane + 32 : lane);
+                if (sub <= kgs - 3) S *= q;
+            }
+            const float ex = __shfl(S, lane < 48 ? lane + 16 : lane);
+            gsuf = sub < kgs - 1 ? ex : 1.f;
+        }
 
         // forward walk: state before each row, dL/dC at sample ends
-        float x = apply(Fx, 0.f);
+        float x = x_in;
         float xbef[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = lr0 + 4 * kg + j;
-            const int bl = r >> kshift, t = r & (K - 1);
-            xbef[j] = t == 0 ? 0.f : x;
-            x = apply(fm[j], x);
-            if (half == 0 && r < ce && t == K - 1) dCl[bl][ln] = dctl[bl][ln] * x;
+            xbef[j] = tj[j] == 0 ? 0.f : x;
+            x = tj[j] == 0 ? beta[j] : gate[j] * x + beta[j];
+            if (half == 0 && r < ce && tj[j] == K - 1) dCl[r >> kshift][ln] = dctl[r >> kshift][ln] * x;
         }
-        // reverse walk: adjoint of each row's output state
-        float m_in = apply(Rx, mu);
+        // reverse walk: adjoint of each row's output state, entering the
+        // lane's last row as lambda_K of its sample times the later gates
+        float m_in = laml[(lr0 + 4 * kg + 3) >> kshift][ln] * gsuf;
         f4 dA4, dB4;
 #pragma unroll
         for (int j = 3; j >= 0; --j) {
@@ -1326,7 +1356,11 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             const float gt = gate[j];
             dB4[j] = v ? m_in : 0.f;
             dA4[j] = v ? m_in * xbef[j] * (gt * (1.f - gt)) : 0.f;
-            m_in = apply(rm[j], m_in);
+            if (j > 0) {
+                // a sample starts at row j (K < 4): the row before ends the previous one
+                const int bp = (r >> kshift) - 1;
+                m_in = tj[j] == 0 ? laml[bp > 0 ? bp : 0][ln] : gt * m_in;
+            }
         }
 
         // weight-gradient contraction of this half over the block's 16 rows

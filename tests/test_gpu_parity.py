@@ -41,6 +41,13 @@ SMALL = [
     (4, 256, 512, 128, "f32", 0.0),   # wide shape, small batch
     (23, 7, 320, 80, "bf16", -1.0),
     (3, 2, 448, 256, "f32", 0.25),    # widest D
+    # K dividing 16 with SH2 <= 256 (the backward's per-block kernel): a
+    # sample spans 4, 2 or 1 lane groups, or a lane holds several samples
+    (37, 16, 256, 16, "f32", 1.0),
+    (29, 4, 128, 32, "f32", -1.0),
+    (45, 2, 192, 16, "bf16", 0.5),
+    (13, 16, 64, 48, "f32", 2.0),
+    (70, 2, 256, 16, "f32", 0.0),
 ]
 
 

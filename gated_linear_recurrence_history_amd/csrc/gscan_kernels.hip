@@ -1012,53 +1012,19 @@ struct BTask {
 };
 
 // ============================================ backward, K dividing 16 ("rows")
-// When K divides 16 every 16-row block holds whole samples, so a wavefront
-// can finish its block alone: projection replay, scans and adjoints as in
-// the kernel above, then the weight-gradient contraction over the block's
-// own 16 rows.  That contraction needs h with rows along the MFMA k index,
+// When K divides 16 every 16-row block holds whole samples, so the block's
+// scans need nothing from other blocks: projection replay, forward and
+// reverse scans, and the weight-gradient contraction over the block's own
+// 16 rows.  That contraction needs h with rows along the MFMA k index,
 // while the row loads put columns along k.  The split block (bf16 high and
 // low planes) goes to a per-wavefront LDS tile right after the split, and
 // ds_read_b64_tr_b16 reads it back transposed: four rows of one column per
 // lane.  Four rows of high parts and the same four rows of low parts make
 // one k = 32 operand [high | low]; its products with [dhigh | dhigh] and
 // [dlow | 0] give the three terms of the split product in two MFMAs.  No
-// transposed reloads, no second split, no LDS exchange between wavefronts.
-// Every wavefront accumulates all SH2 columns; the four sums are added
-// through LDS at the end in a fixed order.  One persistent workgroup per CU;
-// the next chunk's rows (and the next group's h_s2 rows) are requested
-// before the current chunk is computed.
-
-// B[k][n] = (k == 16t + n) in bf16; lane l holds k = 8(l/16) + e, n = l%16
-__device__ __forceinline__ u4 select_operand(int t, int lane)
-{
-    const int e = 16 * t + (lane & 15) - 8 * (lane >> 4);
-    u4 r;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-        r[d] = (e == 2 * d ? 0x3f80u : 0u) | (e == 2 * d + 1 ? 0x3f800000u : 0u);
-    return r;
-}
-
-// columns 16t .. 16t+15 of a split 32-column unit as a contraction A operand:
-// lane l -> column 16t + l%16; k = 8(l/16) + e holds row 4(l/16) + e%4, high
-// part for e < 4 and low part for e >= 4 (high again when LO is false)
-template <bool LO>
-__device__ __forceinline__ u4 transpose_unit(const Split &s, const u4 &sel)
-{
-    const f4 th = mfma_bf(s.hi, sel, zero4());
-    u4 r;
-    r[0] = pack_bf16(th[0], th[1]);
-    r[1] = pack_bf16(th[2], th[3]);
-    if constexpr (LO) {
-        const f4 tl = mfma_bf(s.lo, sel, zero4());
-        r[2] = pack_bf16(tl[0], tl[1]);
-        r[3] = pack_bf16(tl[2], tl[3]);
-    } else {
-        r[2] = r[0];
-        r[3] = r[1];
-    }
-    return r;
-}
+// transposed reloads and no second split.  One persistent workgroup per CU;
+// the next chunk's rows are requested as soon as the current chunk has
+// been split, the next group's h_s2 rows at the start of each step.
 
 typedef short s4v __attribute__((ext_vector_type(4)));
 
@@ -1229,17 +1195,23 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         for (int j = 0; j < 4; ++j) cvp[wave][4 * (llane >> 4) + j][llane & 15] = cp[j];
     };
 
-    auto step = [&](const BTask &cur, PBlk<TIn, NH> &pb, const BTask &nxt,
-                    PBlk<TIn, NH> &pbn) __attribute__((always_inline)) {
+    // cur: this chunk, in pb; nxt: the next one, requested into pb once this
+    // chunk has been split.  One buffer and one copy of the step in the loop:
+    // alternating two buffers by unrolling made the compiler alternate the
+    // MFMA accumulators between two register sets.
+    auto step = [&](const BTask &cur, PBlk<TIn, NH> &pb,
+                    const BTask &nxt) __attribute__((always_inline)) {
         const int nb = samples_of(cur.g);
         const int NR = nb * K;
         const int nch = (NR + kChunkRows - 1) / kChunkRows;
         const int c = cur.c;
         const bool more = nxt.g < groups;
-        // the next group's rows (consumed at this step's end when the next
-        // chunk starts a group) go out first, the next chunk's rows right
-        // after this chunk's projection, once its registers are free
-        if (more && nxt.c == 0) load_group(nxt.g);
+        // the rows of the next chunk's group (consumed at this step's end
+        // when the next chunk starts a group; requested every step, cache
+        // hits otherwise, so that the waits for the older rows of this chunk
+        // stay exact); the next chunk's rows go out right after this chunk's
+        // projection, into the registers it frees
+        load_group(more ? nxt.g : cur.g);
         __syncthreads();  // last step's exchange read; this group's C partials visible
         if (c == 0) {
             // lambda_K = dL/dx_K = d_context * C of the group's samples
@@ -1273,7 +1245,7 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             // keep later units' operand reads from being hoisted here
             __builtin_amdgcn_sched_barrier(0);
         }
-        load_chunk(more ? nxt : cur, pbn);  // this chunk again after the last
+        load_chunk(more ? nxt : cur, pb);  // this chunk again after the last
         xch[wave][0][lane] = pA;
         xch[wave][1][lane] = pB;
         __syncthreads();
@@ -1412,7 +1384,7 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         }
     };
 
-    PBlk<TIn, NH> pA, pB;
+    PBlk<TIn, NH> pA;
     BTask cur = {rho, 0, 0, 0};
     {
         WStage<NQ, kThreads2> wst;
@@ -1425,12 +1397,8 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     __syncthreads();  // weights staged
     if (cur.g < groups) use_group(samples_of(cur.g));
     while (cur.g < groups) {
-        BTask nxt = advance(cur);
-        step(cur, pA, nxt, pB);
-        if (nxt.g >= groups) break;
-        cur = nxt;
-        nxt = advance(cur);
-        step(cur, pB, nxt, pA);
+        const BTask nxt = advance(cur);
+        step(cur, pA, nxt);
         cur = nxt;
     }
 

@@ -195,7 +195,9 @@ def main():
     # dominant kernel against HBM (its MFMA time, 3 bf16 products per fp32
     # product at the bf16 peak, is far below its HBM time)
     if k_bwd >= k_fwd:
-        kname, kus, kbytes, kflops = "gscan_bwd_kernel", k_bwd, w.bwd_bytes(), w.bwd_flops()
+        # K dividing 16 with SH2 <= 256 runs the per-block backward kernel
+        bname = "gscan_bwd_rows_kernel" if 16 % w.K == 0 and w.SH2 <= 256 else "gscan_bwd_kernel"
+        kname, kus, kbytes, kflops = bname, k_bwd, w.bwd_bytes(), w.bwd_flops()
     else:
         kname, kus, kbytes, kflops = "gscan_fwd_kernel", k_fwd, w.fwd_bytes(), w.fwd_flops()
     t_hbm_us = kbytes / (HBM_PEAK_GBS * 1e9) * 1e6
@@ -225,7 +227,7 @@ def main():
         "hbm_frac": round(hbm_frac, 4),
         "hbm_GBs_fwd_bwd": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
-        "kernels_us": {"gscan_fwd_kernel": round(k_fwd, 3), "gscan_bwd_kernel": round(k_bwd, 3),
+        "kernels_us": {"gscan_fwd_kernel": round(k_fwd, 3), "backward_phase1": round(k_bwd, 3),
                        "gscan_reduce_kernel": round(k_red, 3)},
         "roofline": roof,
     }

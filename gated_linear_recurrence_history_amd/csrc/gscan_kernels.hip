@@ -123,13 +123,15 @@ template <typename T, int NQ> struct PBlk;
 template <int NQ> struct PBlk<float, NQ> {
     static constexpr bool kLo = true;
     f4 v[NQ][2];
+    __device__ __forceinline__ void load_unit(const float *__restrict__ row, int kg, int q)
+    {
+        v[q][0] = *reinterpret_cast<const f4 *>(row + 32 * q + 8 * kg);
+        v[q][1] = *reinterpret_cast<const f4 *>(row + 32 * q + 8 * kg + 4);
+    }
     __device__ __forceinline__ void load(const float *__restrict__ row, int kg)
     {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            v[q][0] = *reinterpret_cast<const f4 *>(row + 32 * q + 8 * kg);
-            v[q][1] = *reinterpret_cast<const f4 *>(row + 32 * q + 8 * kg + 4);
-        }
+        for (int q = 0; q < NQ; ++q) load_unit(row, kg, q);
     }
     __device__ __forceinline__ Split op(int q) const
     {
@@ -142,10 +144,14 @@ template <int NQ> struct PBlk<float, NQ> {
 template <int NQ> struct PBlk<uint16_t, NQ> {
     static constexpr bool kLo = false;  // bf16 storage is exact in hi
     u4 v[NQ];
+    __device__ __forceinline__ void load_unit(const uint16_t *__restrict__ row, int kg, int q)
+    {
+        v[q] = *reinterpret_cast<const u4 *>(row + 32 * q + 8 * kg);
+    }
     __device__ __forceinline__ void load(const uint16_t *__restrict__ row, int kg)
     {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) v[q] = *reinterpret_cast<const u4 *>(row + 32 * q + 8 * kg);
+        for (int q = 0; q < NQ; ++q) load_unit(row, kg, q);
     }
     __device__ __forceinline__ Split op(int q) const
     {
@@ -1152,11 +1158,12 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         return n;
     };
     // this wavefront's half of the projection rows of a chunk (block blk)
-    auto load_chunk = [&](const BTask &t, PBlk<TIn, NH> &pb) {
+    auto chunk_row = [&](const BTask &t) {
         const int nr = samples_of(t.g) * K;
         const int r = t.c * kChunkRows + kBlockRows * blk + ln;
-        pb.load(hh + t.g * kGroupSamples * K * SH2 + (uint32_t)((r < nr ? r : nr - 1) * SH2 + HC * half), kg);
+        return hh + t.g * kGroupSamples * K * SH2 + (uint32_t)((r < nr ? r : nr - 1) * SH2 + HC * half);
     };
+    auto load_chunk = [&](const BTask &t, PBlk<TIn, NH> &pb) { pb.load(chunk_row(t), kg); };
     // a group's h_s2 unit `wave` (C projection, dW_C) and d_context slice.
     // Loads here and in load_chunk are unconditional (clamped addresses) so
     // that every path issues the same loads and the waits for older ones
@@ -1231,11 +1238,15 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         const int lr0 = cb + kBlockRows * blk;
 
         // split this half once: projection from registers, contraction
-        // transposed from the wavefront's LDS tile
+        // transposed from the wavefront's LDS tile.  Each unit's registers
+        // take the next chunk's unit as soon as it has been split (this chunk
+        // again after the last).
+        const TIn *__restrict__ nrow = chunk_row(more ? nxt : cur);
         f4 pA = zero4(), pB = zero4();
 #pragma unroll
         for (int u = 0; u < NH; ++u) {
             const Split sp = pb.op(u);
+            pb.load_unit(nrow, kg, u);
             *reinterpret_cast<u4 *>(tile + ln * kPitch + 32 * u + 8 * kg) = sp.hi;
             if constexpr (LO)
                 *reinterpret_cast<u4 *>(tile + (16 + ln) * kPitch + 32 * u + 8 * kg) = sp.lo;
@@ -1245,7 +1256,6 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             // keep later units' operand reads from being hoisted here
             __builtin_amdgcn_sched_barrier(0);
         }
-        load_chunk(more ? nxt : cur, pb);  // this chunk again after the last
         xch[wave][0][lane] = pA;
         xch[wave][1][lane] = pB;
         __syncthreads();

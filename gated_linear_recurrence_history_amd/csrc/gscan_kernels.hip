@@ -1045,6 +1045,27 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t *p)
     return __builtin_bit_cast(uint2, v);
 }
 
+// Cross-row exchanges of a wavefront (rows of 16 lanes).  pair_rows gives
+// every lane the values of the even and the odd row of its row pair (0-1 or
+// 2-3); half_rows gives rows r and r + 2 the value of row r % 2 (.lo) and of
+// row 2 + r % 2 (.hi).  Call them with every lane active (never under a
+// lane-dependent condition): a lane reads the other row's register.
+struct RowVals {
+    float lo, hi;
+};
+
+__device__ __forceinline__ RowVals pair_rows(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+__device__ __forceinline__ RowVals half_rows(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // B operands for four rows 4(l/16) + j of one state: [dhigh | dhigh] and
 // [dlow | 0] (LO), or [dhigh | dlow] when the A operand is [high | high]
 struct GradOp {
@@ -1219,6 +1240,8 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         // stay exact); the next chunk's rows go out right after this chunk's
         // projection, into the registers it frees
         load_group(more ? nxt.g : cur.g);
+        // the first unit's weight operands (the rest follow one unit ahead)
+        Split wAn = wop(Wl, half * NH, 0, lane), wBn = wop(Wl, half * NH, 1, lane);
         __syncthreads();  // last step's exchange read; this group's C partials visible
         if (c == 0) {
             // lambda_K = dL/dx_K = d_context * C of the group's samples
@@ -1241,19 +1264,25 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         // transposed from the wavefront's LDS tile.  Each unit's registers
         // take the next chunk's unit as soon as it has been split (this chunk
         // again after the last).
+        // The weight operands of unit u + 1 are read while unit u is split
+        // and projected, so no LDS read latency sits between two units.
         const TIn *__restrict__ nrow = chunk_row(more ? nxt : cur);
         f4 pA = zero4(), pB = zero4();
 #pragma unroll
         for (int u = 0; u < NH; ++u) {
+            const Split wA = wAn, wB = wBn;
+            if (u + 1 < NH) {
+                wAn = wop(Wl, half * NH + u + 1, 0, lane);
+                wBn = wop(Wl, half * NH + u + 1, 1, lane);
+            }
             const Split sp = pb.op(u);
             pb.load_unit(nrow, kg, u);
             *reinterpret_cast<u4 *>(tile + ln * kPitch + 32 * u + 8 * kg) = sp.hi;
             if constexpr (LO)
                 *reinterpret_cast<u4 *>(tile + (16 + ln) * kPitch + 32 * u + 8 * kg) = sp.lo;
-            const int q = half * NH + u;
-            pA = mfma3<LO>(sp, wop(Wl, q, 0, lane), pA);
-            pB = mfma3<LO>(sp, wop(Wl, q, 1, lane), pB);
-            // keep later units' operand reads from being hoisted here
+            pA = mfma3<LO>(sp, wA, pA);
+            pB = mfma3<LO>(sp, wB, pB);
+            // keep later units' operand reads from being hoisted further
             __builtin_amdgcn_sched_barrier(0);
         }
         xch[wave][0][lane] = pA;
@@ -1279,42 +1308,56 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             gate[j] = v ? gt : 1.f;
             beta[j] = v ? aB[j] : 0.f;
         }
-        const int kgs = K >> 2;                       // lane groups per sample (K >= 8: 2 or 4)
-        const int sub = kgs > 1 ? (kg & (kgs - 1)) : 0;  // lane group within its sample
+        // LDS values of the walks, read up front (clamped rows; used only
+        // where the row is valid): d_context at each row's sample, lambda_K
+        // of the sample of the lane's last row and of the sample before each
+        // row (a sample starting inside the lane when K < 4)
+        float dcv[4], lprev[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int sj = (lr0 + 4 * kg + j) >> kshift;
+            dcv[j] = dctl[sj < 15 ? sj : 15][ln];
+            lprev[j] = laml[sj - 1 < 0 ? 0 : (sj - 1 < 15 ? sj - 1 : 15)][ln];
+        }
+        const int s3 = (lr0 + 4 * kg + 3) >> kshift;
+        const float llast = laml[s3 < 15 ? s3 : 15][ln];
+
+        const int kgs = K >> 2;  // lane groups per sample (K >= 8: 2 or 4)
+        const bool odd = kg & 1;
         const float G = gate[0] * gate[1] * gate[2] * gate[3];
         float x_in = 0.f, gsuf = 1.f;  // state entering the lane; gates of later groups
         if (kgs > 1) {
-            // forward: affine map of the lane's rows, prefix over the sample's groups
+            // forward: affine map (M, C) of the lane's rows, composed over the
+            // sample's lane groups; first within pairs of groups, then (K = 16)
+            // the second pair after the first pair's total
             float M = G, C = beta[0];
             C = gate[1] * C + beta[1];
             C = gate[2] * C + beta[2];
             C = gate[3] * C + beta[3];
-            float pM = __shfl(M, lane >= 16 ? lane - 16 : lane);
-            float pC = __shfl(C, lane >= 16 ? lane - 16 : lane);
-            if (sub >= 1) {
-                C = M * pC + C;
-                M = M * pM;
+            const RowVals pm = pair_rows(M), pc = pair_rows(C);
+            if (odd) {
+                C = M * pc.lo + C;
+                M = M * pm.lo;
             }
-            if (kgs > 2) {
-                pM = __shfl(M, lane >= 32 ? lane - 32 : lane);
-                pC = __shfl(C, lane >= 32 ? lane - 32 : lane);
-                if (sub >= 2) {
-                    C = M * pC + C;
-                    M = M * pM;
-                }
-            }
-            const float e = __shfl(C, lane >= 16 ? lane - 16 : lane);
-            x_in = sub >= 1 ? e : 0.f;
             // reverse: product of the gates of the sample's later groups
-            float S = G;
-            float q = __shfl(S, lane < 48 ? lane + 16 : lane);
-            if (sub <= kgs - 2) S *= q;
+            const RowVals pg = pair_rows(G);
+            gsuf = odd ? 1.f : pg.hi;
             if (kgs > 2) {
-                q = __shfl(S, lane < 32 ? lane + 32 : lane);
-                if (sub <= kgs - 3) S *= q;
+                // the first pair's total (held by its odd group) into rows 2-3
+                const float tM = pair_rows(M).hi, tC = pair_rows(C).hi;
+                const float fM = half_rows(tM).lo, fC = half_rows(tC).lo;
+                const bool second = kg >= 2;
+                if (second) {
+                    C = M * fC + C;
+                    M = M * fM;
+                }
+                const float cl = pair_rows(C).lo;  // (all lanes take part)
+                x_in = odd ? cl : (second ? fC : 0.f);
+                const float hP = half_rows(pg.lo * pg.hi).hi;  // the second pair's gates
+                if (!second) gsuf *= hP;
+            } else {
+                x_in = odd ? pc.lo : 0.f;
             }
-            const float ex = __shfl(S, lane < 48 ? lane + 16 : lane);
-            gsuf = sub < kgs - 1 ? ex : 1.f;
         }
 
         // forward walk: state before each row, dL/dC at sample ends
@@ -1325,11 +1368,11 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             const int r = lr0 + 4 * kg + j;
             xbef[j] = tj[j] == 0 ? 0.f : x;
             x = tj[j] == 0 ? beta[j] : gate[j] * x + beta[j];
-            if (half == 0 && r < ce && tj[j] == K - 1) dCl[r >> kshift][ln] = dctl[r >> kshift][ln] * x;
+            if (half == 0 && r < ce && tj[j] == K - 1) dCl[r >> kshift][ln] = dcv[j] * x;
         }
         // reverse walk: adjoint of each row's output state, entering the
         // lane's last row as lambda_K of its sample times the later gates
-        float m_in = laml[(lr0 + 4 * kg + 3) >> kshift][ln] * gsuf;
+        float m_in = llast * gsuf;
         f4 dA4, dB4;
 #pragma unroll
         for (int j = 3; j >= 0; --j) {
@@ -1338,11 +1381,8 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             const float gt = gate[j];
             dB4[j] = v ? m_in : 0.f;
             dA4[j] = v ? m_in * xbef[j] * (gt * (1.f - gt)) : 0.f;
-            if (j > 0) {
-                // a sample starts at row j (K < 4): the row before ends the previous one
-                const int bp = (r >> kshift) - 1;
-                m_in = tj[j] == 0 ? laml[bp > 0 ? bp : 0][ln] : gt * m_in;
-            }
+            // a sample starts at row j (K < 4): the row before ends the previous one
+            if (j > 0) m_in = tj[j] == 0 ? lprev[j] : gt * m_in;
         }
 
         // weight-gradient contraction of this half over the block's 16 rows

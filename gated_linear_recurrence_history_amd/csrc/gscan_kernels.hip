@@ -212,46 +212,75 @@ __device__ __forceinline__ float apply(const Aff &a, float x)
     return a.r ? a.c : a.m * x + a.c;
 }
 
-__device__ __forceinline__ Aff shfl_aff(const Aff &a, int src)
+// Cross-row exchanges of a wavefront (rows of 16 lanes).  pair_rows gives
+// every lane the values of the even and the odd row of its row pair (0-1 or
+// 2-3); half_rows gives rows r and r + 2 the value of row r % 2 (.lo) and of
+// row 2 + r % 2 (.hi).  Call them with every lane active (never under a
+// lane-dependent condition): a lane reads the other row's register.
+struct RowVals {
+    float lo, hi;
+};
+
+__device__ __forceinline__ RowVals pair_rows(float x)
 {
-    Aff o;
-    o.m = __shfl(a.m, src);
-    o.c = __shfl(a.c, src);
-    o.r = __shfl(a.r, src);
-    return o;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
-// Prefix over the four lane groups g = lane/16 (ascending): the composite of
-// groups < g (exclusive) and of all four groups (total).
+__device__ __forceinline__ RowVals half_rows(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+struct AffRows {
+    Aff lo, hi;
+};
+
+__device__ __forceinline__ AffRows pair_aff(const Aff &a)
+{
+    const RowVals m = pair_rows(a.m), c = pair_rows(a.c), r = pair_rows(__int_as_float(a.r));
+    return {{m.lo, c.lo, __float_as_int(r.lo)}, {m.hi, c.hi, __float_as_int(r.hi)}};
+}
+
+__device__ __forceinline__ AffRows half_aff(const Aff &a)
+{
+    const RowVals m = half_rows(a.m), c = half_rows(a.c), r = half_rows(__int_as_float(a.r));
+    return {{m.lo, c.lo, __float_as_int(r.lo)}, {m.hi, c.hi, __float_as_int(r.hi)}};
+}
+
+// Prefix over the four lane groups (rows) of a wavefront, lower rows first:
+// within row pairs, then the second pair after the first pair's total.
+// excl: composition of the rows before; total: of all four rows.
 __device__ __forceinline__ void scan_up(const Aff &mine, int lane, Aff &excl, Aff &total)
 {
     const int kg = lane >> 4;
-    Aff p = shfl_aff(mine, lane - 16 < 0 ? lane : lane - 16);
-    if (kg < 1) p = aff_id();
-    const Aff s1 = compose(mine, p);
-    Aff q = shfl_aff(s1, lane - 32 < 0 ? lane : lane - 32);
-    if (kg < 2) q = aff_id();
-    const Aff s2 = compose(s1, q);  // inclusive prefix
-    Aff e = shfl_aff(s2, lane - 16 < 0 ? lane : lane - 16);
-    if (kg < 1) e = aff_id();
-    excl = e;
-    total = shfl_aff(s2, 48 + (lane & 15));
+    const bool odd = kg & 1, second = kg >= 2;
+    const AffRows p1 = pair_aff(mine);
+    const Aff s1 = odd ? compose(mine, p1.lo) : mine;
+    const AffRows t1 = pair_aff(s1);     // .hi: the pair's composition
+    const AffRows h1 = half_aff(t1.hi);  // .lo: the first pair's, in rows 2-3
+    const Aff s2 = second ? compose(s1, h1.lo) : s1;  // inclusive prefix
+    const AffRows p2 = pair_aff(s2);
+    const AffRows h2 = half_aff(p2.hi);
+    excl = odd ? p2.lo : (second ? h2.lo : aff_id());
+    total = second ? p2.hi : h2.hi;
 }
 
-// Suffix over the lane groups (descending: group 3 applied first).
+// Suffix over the four rows, higher rows first (mirror of scan_up).
 __device__ __forceinline__ void scan_down(const Aff &mine, int lane, Aff &excl, Aff &total)
 {
     const int kg = lane >> 4;
-    Aff p = shfl_aff(mine, lane + 16 > 63 ? lane : lane + 16);
-    if (kg > 2) p = aff_id();
-    const Aff s1 = compose(mine, p);
-    Aff q = shfl_aff(s1, lane + 32 > 63 ? lane : lane + 32);
-    if (kg > 1) q = aff_id();
-    const Aff s2 = compose(s1, q);  // inclusive suffix
-    Aff e = shfl_aff(s2, lane + 16 > 63 ? lane : lane + 16);
-    if (kg > 2) e = aff_id();
-    excl = e;
-    total = shfl_aff(s2, lane & 15);
+    const bool odd = kg & 1, first = kg < 2;
+    const AffRows p1 = pair_aff(mine);
+    const Aff s1 = odd ? mine : compose(mine, p1.hi);
+    const AffRows t1 = pair_aff(s1);     // .lo: the pair's composition
+    const AffRows h1 = half_aff(t1.lo);  // .hi: the second pair's, in rows 0-1
+    const Aff s2 = first ? compose(s1, h1.hi) : s1;  // inclusive suffix
+    const AffRows p2 = pair_aff(s2);
+    const AffRows h2 = half_aff(p2.lo);
+    excl = odd ? (first ? h2.hi : aff_id()) : p2.hi;
+    total = first ? p2.lo : h2.lo;
 }
 
 __device__ __forceinline__ float sigmoid(float a)
@@ -406,18 +435,23 @@ __device__ __forceinline__ void project(const PBlk<TIn, NQ> (&blk)[NB], const u4
         aA[b] = zero4();
         aB[b] = zero4();
     }
+    // the weight operands of unit q + 1 are read while unit q is projected
+    Split wan = wop(Wl, 0, 0, lane), wbn = wop(Wl, 0, 1, lane);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const Split wa = wop(Wl, q, 0, lane);
-        const Split wb = wop(Wl, q, 1, lane);
+        const Split wa = wan, wb = wbn;
+        if (q + 1 < NQ) {
+            wan = wop(Wl, q + 1, 0, lane);
+            wbn = wop(Wl, q + 1, 1, lane);
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const Split h = blk[b].op(q);
             aA[b] = mfma3<LO>(h, wa, aA[b]);
             aB[b] = mfma3<LO>(h, wb, aB[b]);
         }
-        // keep the weight-operand reads of later units from being hoisted here
-        // (they would pin NQ x 16 registers next to the in-flight rows)
+        // keep the weight-operand reads of later units from being hoisted
+        // further (they would pin NQ x 16 registers next to the in-flight rows)
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -1043,27 +1077,6 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t *p)
     const s4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s4v *)(p));
     return __builtin_bit_cast(uint2, v);
-}
-
-// Cross-row exchanges of a wavefront (rows of 16 lanes).  pair_rows gives
-// every lane the values of the even and the odd row of its row pair (0-1 or
-// 2-3); half_rows gives rows r and r + 2 the value of row r % 2 (.lo) and of
-// row 2 + r % 2 (.hi).  Call them with every lane active (never under a
-// lane-dependent condition): a lane reads the other row's register.
-struct RowVals {
-    float lo, hi;
-};
-
-__device__ __forceinline__ RowVals pair_rows(float x)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-
-__device__ __forceinline__ RowVals half_rows(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
 // B operands for four rows 4(l/16) + j of one state: [dhigh | dhigh] and

@@ -99,7 +99,10 @@ __device__ __forceinline__ Split split8(const float (&v)[8])
     Split s;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t h = pack_bf16(v[2 * i], v[2 * i + 1]);
+        uint32_t h = pack_bf16(v[2 * i], v[2 * i + 1]);
+        // opaque, so the low element's high part is taken from the pair
+        // (one shift) instead of being converted a second time
+        asm("" : "+v"(h));
         s.hi[i] = h;
         s.lo[i] = pack_bf16(v[2 * i] - bf_lo(h), v[2 * i + 1] - bf_hi(h));
     }

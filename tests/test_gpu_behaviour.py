@@ -92,3 +92,48 @@ def test_errors_leave_outputs_untouched():
     assert torch.all(out == 3.0)
     with pytest.raises(ValueError):
         gs.forward(bad_h, t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K)
+
+
+def test_graph_replays():
+    """Forward and backward captured once in a HIP graph and replayed with
+    new inputs copied in between (eager work and synchronisation between
+    replays): every replay equals an eager call on its inputs."""
+    w = workload(2048, 8, 256, 16, seed=21)
+    print("case graph replays", flush=True)
+    x = synth.make_inputs(w)
+    t = device_inputs(x)
+    h = t["h_history"].clone()
+    d = t["d_context"].clone()
+    n = binding.backward_workspace_bytes(w.B, w.K, w.SH2, w.D)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    ctx = torch.empty((w.B, w.D), device=DEV)
+    out = tuple(torch.empty((w.SH2, w.D), device=DEV) for _ in range(3))
+
+    def step():
+        gs.forward(h, t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K, 0.0, out=ctx)
+        gs.backward(h, t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K, d, 0.0, out=out,
+                    workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager call before capture
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        h.copy_(t["h_history"] * (1.0 - 0.25 * i))
+        d.copy_(t["d_context"] * (1.0 + 0.5 * i) - 0.25 * i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_ctx = ctx.cpu().numpy()
+        got = tuple(o.cpu().numpy() for o in out)
+        ref_ctx = gpu_forward({**t, "h_history": h}, w.K, 0.0)
+        ref = gpu_backward({**t, "h_history": h}, w.K, 0.0, d_context=d)
+        assert np.array_equal(got_ctx, ref_ctx), i
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b), i

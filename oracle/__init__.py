@@ -4,7 +4,7 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
 import this package.  The product path (the HIP library and its binding)
 never touches it.
 
-`forward` / `backward` widen every input exactly to float64 (float32 as is,
+`forward` / `backward` / `backward_inputs` widen every input exactly to float64 (float32 as is,
 bfloat16 given as raw uint16 bits by zero-extending the low mantissa) and
 call plain double-precision C loops (gscan_oracle.c).
 """
@@ -35,6 +35,9 @@ def _load():
         lib.oracle_backward.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
                                         ctypes.c_double, dp, dp, dp, dp]
         lib.oracle_backward.restype = None
+        lib.oracle_backward_inputs.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                               ctypes.c_double, dp, dp, dp]
+        lib.oracle_backward_inputs.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -91,6 +94,20 @@ def backward(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: float =
                             wc.ctypes.data, B, K, SH2, D, float(a_shift), dc.ctypes.data,
                             dwa.ctypes.data, dwb.ctypes.data, dwc.ctypes.data)
     return dwa, dwb, dwc
+
+
+def backward_inputs(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: float = 0.0):
+    """(d_h_history [B*K, SH2], d_h_s2 [B, SH2]) float64, for L = sum(d_context * context)."""
+    h, hs, wa, wb, wc, dc = (widen(a) for a in (h_history, h_s2, W_A, W_B, W_C, d_context))
+    B, SH2, D = _shapes(h, hs, wa, K)
+    if dc.shape != (B, D):
+        raise ValueError(f"d_context shape {dc.shape} != {(B, D)}")
+    dh = np.empty((B * K, SH2), dtype=np.float64)
+    dhs = np.empty((B, SH2), dtype=np.float64)
+    _load().oracle_backward_inputs(h.ctypes.data, hs.ctypes.data, wa.ctypes.data,
+                                   wb.ctypes.data, wc.ctypes.data, B, K, SH2, D, float(a_shift),
+                                   dc.ctypes.data, dh.ctypes.data, dhs.ctypes.data)
+    return dh, dhs
 
 
 def sample_rows(inputs: dict, K: int, samples) -> dict:

@@ -218,3 +218,87 @@ void oracle_backward(const double *h_history, const double *h_s2,
     }
     free(part);
 }
+
+/*
+ * Input gradients: the chain rule through the projections of Step 1 (the
+ * spec's backward lists only the weight gradients; these are the gradients
+ * a layer below the scan would receive):
+ *   d_h_history[b*K+t, i] = sum_s dA_t[s] * W_A[i, s] + dB_t[s] * W_B[i, s]
+ *   d_h_s2[b, i]          = sum_s dC[s] * W_C[i, s]
+ * with dA_t = dL/dA_vals, dB_t = dL/dB_vals and dC = dL/dC_vals from the same
+ * replay and reverse scan as oracle_backward.  Each sample is independent.
+ */
+void oracle_backward_inputs(const double *h_history, const double *h_s2,
+                            const double *W_A, const double *W_B, const double *W_C,
+                            int64_t B, int64_t K, int64_t SH2, int64_t D, double a_shift,
+                            const double *d_context, double *d_h_history, double *d_h_s2)
+{
+#pragma omp parallel
+    {
+        double *Cv = (double *)malloc(sizeof(double) * D);
+        double *Av = (double *)malloc(sizeof(double) * D);
+        double *Bv = (double *)malloc(sizeof(double) * D);
+        double *xs = (double *)malloc(sizeof(double) * (K + 1) * D); /* x_0..x_K */
+        double *gs = (double *)malloc(sizeof(double) * K * D);       /* g_0..g_{K-1} */
+        double *adj = (double *)malloc(sizeof(double) * D); /* dL/dx_{t+1} */
+        double *dA = (double *)malloc(sizeof(double) * D);
+        double *dB = (double *)malloc(sizeof(double) * D);
+        double *dC = (double *)malloc(sizeof(double) * D);
+        int64_t b;
+#pragma omp for schedule(dynamic, 16)
+        for (b = 0; b < B; ++b) {
+            int64_t t, s, ii;
+            /* replay */
+            project(h_s2 + b * SH2, W_C, SH2, D, Cv);
+            for (s = 0; s < D; ++s)
+                xs[s] = 0.0;
+            for (t = 0; t < K; ++t) {
+                const double *row = h_history + (b * K + t) * SH2;
+                project(row, W_A, SH2, D, Av);
+                project(row, W_B, SH2, D, Bv);
+                for (s = 0; s < D; ++s) {
+                    const double gt = sigmoid(a_shift + Av[s]);
+                    gs[t * D + s] = gt;
+                    xs[(t + 1) * D + s] = gt * xs[t * D + s] + Bv[s];
+                }
+            }
+            /* reverse scan */
+            for (s = 0; s < D; ++s) {
+                adj[s] = d_context[b * D + s] * Cv[s];
+                dC[s] = xs[K * D + s] * d_context[b * D + s];
+            }
+            for (t = K - 1; t >= 0; --t) {
+                double *out = d_h_history + (b * K + t) * SH2;
+                for (s = 0; s < D; ++s) {
+                    const double gt = gs[t * D + s];
+                    dB[s] = adj[s];
+                    dA[s] = adj[s] * xs[t * D + s] * gt * (1.0 - gt);
+                    adj[s] = gt * adj[s];
+                }
+                /* row t of d_gate @ W_A^T + d_x @ W_B^T */
+                for (ii = 0; ii < SH2; ++ii) {
+                    double v = 0.0;
+                    for (s = 0; s < D; ++s)
+                        v += dA[s] * W_A[ii * D + s] + dB[s] * W_B[ii * D + s];
+                    out[ii] = v;
+                }
+            }
+            /* row b of dC @ W_C^T */
+            for (ii = 0; ii < SH2; ++ii) {
+                double v = 0.0;
+                for (s = 0; s < D; ++s)
+                    v += dC[s] * W_C[ii * D + s];
+                d_h_s2[b * SH2 + ii] = v;
+            }
+        }
+        free(Cv);
+        free(Av);
+        free(Bv);
+        free(xs);
+        free(gs);
+        free(adj);
+        free(dA);
+        free(dB);
+        free(dC);
+    }
+}

@@ -32,6 +32,23 @@ MUTANTS = {
     "a_shift_ignored": ("sigmoid(Av[s] + a_shift);\n                    gs", "sigmoid(Av[s]);\n                    gs"),
     "dWC_wrong_row": ("pC[ii * D + s] += h_s2[b * SH2 + ii] * dC[s];",
                       "pC[ii * D + s] += h_s2[(b + 1) % B * SH2 + ii] * dC[s];"),
+    # input gradients
+    "dh_weights_swapped": ("v += dA[s] * W_A[ii * D + s] + dB[s] * W_B[ii * D + s];",
+                           "v += dA[s] * W_B[ii * D + s] + dB[s] * W_A[ii * D + s];"),
+    "dh_drops_gate_term": ("v += dA[s] * W_A[ii * D + s] + dB[s] * W_B[ii * D + s];",
+                           "v += dB[s] * W_B[ii * D + s];"),
+    "dh_transposed_weight": ("v += dA[s] * W_A[ii * D + s] + dB[s] * W_B[ii * D + s];",
+                             "v += dA[s] * W_A[(ii * D + s) % SH2 * D + (ii * D + s) / SH2]"
+                             " + dB[s] * W_B[(ii * D + s) % SH2 * D + (ii * D + s) / SH2];"),
+    "dh_rows_reversed": ("double *out = d_h_history + (b * K + t) * SH2;",
+                         "double *out = d_h_history + (b * K + (K - 1 - t)) * SH2;"),
+    "dh_reverse_drops_gate": ("adj[s] = gt * adj[s];", "adj[s] = adj[s];"),
+    "dh_dA_drops_state": ("dA[s] = adj[s] * xs[t * D + s] * gt * (1.0 - gt);",
+                          "dA[s] = adj[s] * gt * (1.0 - gt);"),
+    "dhs2_literal_upstream": ("dC[s] = xs[K * D + s] * d_context[b * D + s];",
+                              "dC[s] = d_context[b * D + s];"),
+    "dhs2_wrong_weight": ("v += dC[s] * W_C[ii * D + s];", "v += dC[s] * W_B[ii * D + s];"),
+    "dh_a_shift_ignored": ("sigmoid(a_shift + Av[s]);", "sigmoid(Av[s]);"),
 }
 
 
@@ -43,6 +60,11 @@ def _pins():
     yield lambda: pins.test_euler_homogeneity(2.0)
     for a in (-3.0, 0.0, 2.0):
         yield lambda a=a: pins.test_central_finite_differences(a)
+    yield lambda: pins.test_input_grad_gate_zero_closed_form(5, 8, 64, 16)
+    yield lambda: pins.test_input_grad_euler_identities(2.0)
+    yield lambda: pins.test_input_grad_k1_and_linearity()
+    for a in (-3.0, 0.0, 2.0):
+        yield lambda a=a: pins.test_input_grad_central_finite_differences(a)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -57,7 +79,8 @@ def test_mutant_is_caught(name, tmp_path):
                     str(lib_path), "-lm"], check=True)
     real = oracle._load()
     mut = ctypes.CDLL(str(lib_path))
-    for fn in ("oracle_forward", "oracle_backward", "oracle_max_threads", "oracle_set_threads"):
+    for fn in ("oracle_forward", "oracle_backward", "oracle_backward_inputs", "oracle_max_threads",
+               "oracle_set_threads"):
         getattr(mut, fn).argtypes = getattr(real, fn).argtypes
         getattr(mut, fn).restype = getattr(real, fn).restype
     caught = False

@@ -193,3 +193,91 @@ def test_bf16_widening_is_exact():
     got = oracle.widen(bits)
     assert got[0] == 1.0 and got[1] == -2.0 and got[2] == 1.0 + 2.0 ** -7
     assert got[3] == 0.0 and np.signbit(got[4]) and got[5] == float.fromhex("0x1.fep127")
+
+
+# ----------------------------------------------------------- input gradients
+def _bin(x, K, a_shift=0.0, d=None):
+    d = x["d_context"] if d is None else d
+    return oracle.backward_inputs(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], K,
+                                  d, a_shift)
+
+
+@pytest.mark.parametrize("a_shift", [-3.0, 0.0, 2.0])
+def test_input_grad_central_finite_differences(a_shift):
+    # Every entry of h_history and h_s2 of a deliberately unaligned shape.
+    B, K, SH2, D = 3, 4, 5, 3
+    x = _inputs(B, K, SH2, D, 19)
+    dh, dhs = _bin(x, K, a_shift)
+    eps = 1e-6
+
+    def loss(y):
+        return float(np.sum(y["d_context"] * _fwd(y, K, a_shift)))
+
+    for name, grad in (("h_history", dh), ("h_s2", dhs)):
+        rows, cols = x[name].shape
+        for r in range(rows):
+            for i in range(cols):
+                yp = dict(x)
+                ym = dict(x)
+                hp = x[name].copy()
+                hm = x[name].copy()
+                hp[r, i] += eps
+                hm[r, i] -= eps
+                yp[name] = hp
+                ym[name] = hm
+                fd = (loss(yp) - loss(ym)) / (2 * eps)
+                an = grad[r, i]
+                assert abs(fd - an) <= 1e-7 * (1 + abs(an)), (name, r, i, fd, an)
+
+
+@pytest.mark.parametrize("B,K,SH2,D", [(5, 8, 64, 16), (3, 3, 7, 5), (2, 1, 4, 3)])
+def test_input_grad_gate_zero_closed_form(B, K, SH2, D):
+    # gate 0: only the last step feeds x_K = B_{K-1}, and dA = 0 everywhere
+    x = _inputs(B, K, SH2, D, 21)
+    a_shift = -1.0e4
+    dh, dhs = _bin(x, K, a_shift)
+    Cv = x["h_s2"] @ x["W_C"]
+    last = np.arange(B) * K + K - 1
+    Bl = x["h_history"][last] @ x["W_B"]
+    dc = x["d_context"]
+    expect = np.zeros_like(dh)
+    expect[last] = (dc * Cv) @ x["W_B"].T
+    assert _rel(dh, expect) < 1e-12
+    assert np.all(dh[np.setdiff1d(np.arange(B * K), last)] == 0.0)
+    assert _rel(dhs, (dc * Bl) @ x["W_C"].T) < 1e-12
+
+
+@pytest.mark.parametrize("a_shift", [-1.0, 0.0, 2.0])
+def test_input_grad_euler_identities(a_shift):
+    # L is linear in h_s2 (C_vals is, x_K does not depend on it): <h_s2, dL/dh_s2> = L.
+    # With W_A = 0 the gates are constants and L is linear in h_history too.
+    B, K, SH2, D = 7, 6, 24, 8
+    x = _inputs(B, K, SH2, D, 23)
+    L = float(np.sum(x["d_context"] * _fwd(x, K, a_shift)))
+    _, dhs = _bin(x, K, a_shift)
+    assert abs(np.sum(x["h_s2"] * dhs) - L) <= 1e-11 * (1 + abs(L))
+    y = dict(x)
+    y["W_A"] = np.zeros_like(x["W_A"])
+    Ly = float(np.sum(y["d_context"] * _fwd(y, K, a_shift)))
+    dh, _ = _bin(y, K, a_shift)
+    assert abs(np.sum(y["h_history"] * dh) - Ly) <= 1e-11 * (1 + abs(Ly))
+
+
+def test_input_grad_k1_and_linearity():
+    # K = 1: x_0 = 0 kills the gate's gradient, d_h = (d_ctx * Cv) W_B^T.
+    B, SH2, D = 6, 16, 4
+    x = _inputs(B, 1, SH2, D, 25)
+    dh, _ = _bin(x, 1, 0.7)
+    Cv = x["h_s2"] @ x["W_C"]
+    assert _rel(dh, (x["d_context"] * Cv) @ x["W_B"].T) < 1e-12
+    # linear in the upstream gradient
+    K = 5
+    y = _inputs(B, K, SH2, D, 26)
+    rng = np.random.default_rng(27)
+    d1 = rng.standard_normal((B, D))
+    d2 = rng.standard_normal((B, D))
+    g1 = _bin(y, K, -0.5, d1)
+    g2 = _bin(y, K, -0.5, d2)
+    g12 = _bin(y, K, -0.5, d1 - 3.0 * d2)
+    for a, b, c in zip(g1, g2, g12):
+        assert _rel(c, a - 3.0 * b) < 1e-12

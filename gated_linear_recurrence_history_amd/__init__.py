@@ -2,11 +2,12 @@
 
 The compute path is the HIP library `libgscan.so` (hand-written gfx950
 kernels behind a C ABI, declared in include/gscan.h); `forward` and
-`backward` are thin ctypes wrappers over it.  There is no CPU fallback.
+`backward` (and `backward_full`, which adds the input gradients) are thin
+ctypes wrappers over it.  There is no CPU fallback.
 """
-from .binding import (forward, backward, backward_workspace_bytes, library_path,  # noqa: F401
-                      GScanError)
+from .binding import (forward, backward, backward_full, backward_workspace_bytes,  # noqa: F401
+                      backward_full_workspace_bytes, library_path, GScanError)
 from . import workloads  # noqa: F401
 
-__all__ = ["forward", "backward", "backward_workspace_bytes", "library_path", "GScanError",
-           "workloads"]
+__all__ = ["forward", "backward", "backward_full", "backward_workspace_bytes",
+           "backward_full_workspace_bytes", "library_path", "GScanError", "workloads"]

@@ -56,6 +56,12 @@ def lib():
         L.gscan_backward_reduce.argtypes = [vp, ctypes.c_size_t, i64, i64, i64, i64, ctypes.c_int,
                                             vp, vp, vp, vp]
         L.gscan_backward_reduce.restype = ctypes.c_int
+        L.gscan_backward_full_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp,
+                                             vp, vp, vp, ctypes.c_int, f32, vp, ctypes.c_size_t,
+                                             vp]
+        L.gscan_backward_full_ex.restype = ctypes.c_int
+        L.gscan_backward_full_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        L.gscan_backward_full_workspace_bytes.restype = ctypes.c_size_t
         L.gscan_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.gscan_backward_workspace_bytes.restype = ctypes.c_size_t
         L.gscan_status_string.argtypes = [ctypes.c_int]
@@ -162,6 +168,48 @@ def backward(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: float =
         out[1].data_ptr(), out[2].data_ptr(), code, float(a_shift), workspace.data_ptr(),
         workspace.numel(), _stream_handle(stream, dev)))
     return out
+
+
+def backward_full_workspace_bytes(B: int, K: int, SH2: int, D: int, bf16: bool = False) -> int:
+    return int(lib().gscan_backward_full_workspace_bytes(B, K, SH2, D,
+                                                         GSCAN_BF16 if bf16 else GSCAN_F32))
+
+
+def backward_full(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: float = 0.0,
+                  out=None, workspace=None, stream=None):
+    """(dW_A, dW_B, dW_C, d_h_history, d_h_s2) for L = sum(d_context * context):
+    the weight gradients of `backward` and the input gradients, float32
+    [SH2, D] x 3, [B*K, SH2] and [B, SH2].  `out` may hold those five tensors."""
+    import torch
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    if (not d_context.is_cuda or d_context.dtype != torch.float32
+            or tuple(d_context.shape) != (B, D) or not d_context.is_contiguous()):
+        raise ValueError("d_context must be a contiguous float32 [B, D] GPU tensor")
+    if out is None:
+        out = tuple(torch.empty((SH2, D), dtype=torch.float32, device=dev) for _ in range(3)) + (
+            torch.empty((B * K, SH2), dtype=torch.float32, device=dev),
+            torch.empty((B, SH2), dtype=torch.float32, device=dev))
+    ws_bytes = int(lib().gscan_backward_full_workspace_bytes(B, K, SH2, D, code))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().gscan_backward_full_ex(
+        h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
+        W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), out[0].data_ptr(),
+        out[1].data_ptr(), out[2].data_ptr(), out[3].data_ptr(), out[4].data_ptr(), code,
+        float(a_shift), workspace.data_ptr(), workspace.numel(), _stream_handle(stream, dev)))
+    return out
+
+
+def prepare_backward_full(h_history, h_s2, W_A, W_B, W_C, K, d_context, out, workspace,
+                          a_shift=0.0, stream=None):
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
+            W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), out[0].data_ptr(),
+            out[1].data_ptr(), out[2].data_ptr(), out[3].data_ptr(), out[4].data_ptr(), code,
+            ctypes.c_float(a_shift), workspace.data_ptr(), workspace.numel(),
+            _stream_handle(stream, dev))
+    return Prepared(lib().gscan_backward_full_ex, args,
+                    (h_history, h_s2, W_A, W_B, W_C, d_context, out, workspace))
 
 
 def backward_partials(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, workspace,

@@ -72,6 +72,22 @@ int check_outputs(const float *dW_A, const float *dW_B, const float *dW_C)
     return GSCAN_OK;
 }
 
+// Workspace of the backward with input gradients: the partials, then
+// dL/dA | dL/dB per row and dL/dC per sample (each 256-byte aligned).
+struct FullLayout {
+    size_t dab = 0, dc = 0, bytes = 0;
+};
+
+FullLayout full_layout(const gscan::Plan &p)
+{
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    FullLayout f;
+    f.dab = up(p.ws_bytes);
+    f.dc = up(f.dab + (size_t)(p.B * p.K) * (size_t)(2 * p.D) * sizeof(float));
+    f.bytes = f.dc + (size_t)p.B * (size_t)p.D * sizeof(float);
+    return f;
+}
+
 int check_workspace(const void *workspace, size_t workspace_bytes, const gscan::Plan &plan)
 {
     if (!workspace) return fail(GSCAN_ERR_INVALID_ARGUMENT, "null workspace");
@@ -144,8 +160,70 @@ int gscan_backward_ex(const void *h_history, const void *h_s2, const float *W_A,
     }
     float *part = static_cast<float *>(ws);
     hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
-                                                   d_context, part, stream);
+                                                   d_context, part, nullptr, nullptr, stream);
     if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
+    if (!workspace) {
+        hipError_t f = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = f;
+    }
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return GSCAN_OK;
+}
+
+size_t gscan_backward_full_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
+                                           gscan_dtype_t in_dtype)
+{
+    if (B <= 0 || K <= 0 || SH2 <= 0 || D <= 0) return 0;
+    gscan::Plan plan;
+    if (!gscan::make_plan(B, K, SH2, D, (int)in_dtype, &plan)) return 0;
+    return full_layout(plan).bytes;
+}
+
+int gscan_backward_full_ex(const void *h_history, const void *h_s2, const float *W_A,
+                           const float *W_B, const float *W_C, int64_t B, int64_t K, int64_t SH2,
+                           int64_t D, const float *d_context, float *dW_A, float *dW_B,
+                           float *dW_C, float *d_h_history, float *d_h_s2,
+                           gscan_dtype_t in_dtype, float a_shift, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream)
+{
+    gscan::Plan plan;
+    int st = check_backward(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, d_context,
+                            (int)in_dtype, &plan);
+    if (st != GSCAN_OK) return st;
+    if ((st = check_outputs(dW_A, dW_B, dW_C)) != GSCAN_OK) return st;
+    if (!d_h_history || !d_h_s2)
+        return fail(GSCAN_ERR_INVALID_ARGUMENT, "null input-gradient pointer");
+    if (!aligned16(d_h_history) || !aligned16(d_h_s2))
+        return fail(GSCAN_ERR_MISALIGNED, "input-gradient pointers must be 16-byte aligned");
+    const FullLayout lay = full_layout(plan);
+    if (workspace) {
+        if (workspace_bytes < lay.bytes)
+            return fail(GSCAN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu",
+                        workspace_bytes, lay.bytes);
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(GSCAN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    }
+    void *ws = workspace;
+    if (!ws) {
+        hipError_t e = hipMallocAsync(&ws, lay.bytes, stream);
+        if (e != hipSuccess)
+            return fail(GSCAN_ERR_HIP, "workspace allocation of %zu bytes failed: %s", lay.bytes,
+                        hipGetErrorString(e));
+    }
+    char *base = static_cast<char *>(ws);
+    float *part = reinterpret_cast<float *>(base);
+    float *dab = reinterpret_cast<float *>(base + lay.dab);
+    float *dc = reinterpret_cast<float *>(base + lay.dc);
+    hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
+                                                   d_context, part, dab, dc, stream);
+    if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
+    if (e == hipSuccess && !plan.bwd_rows_kernel)
+        e = gscan::launch_adjoint(plan, dab, dc, d_context, a_shift, stream);
+    if (e == hipSuccess)
+        e = gscan::launch_dinput(dab, W_A, W_B, D, 2 * D, SH2, B * K, d_h_history, stream);
+    if (e == hipSuccess) e = gscan::launch_dinput(dc, W_C, nullptr, D, D, SH2, B, d_h_s2, stream);
     if (!workspace) {
         hipError_t f = hipFreeAsync(ws, stream);
         if (e == hipSuccess) e = f;
@@ -169,7 +247,7 @@ int gscan_backward_partials(const void *h_history, const void *h_s2, const float
     if ((st = check_workspace(workspace, workspace_bytes, plan)) != GSCAN_OK) return st;
     hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
                                                    d_context, static_cast<float *>(workspace),
-                                                   stream);
+                                                   nullptr, nullptr, stream);
     if (e != hipSuccess)
         return fail(GSCAN_ERR_HIP, "backward phase 1 launch failed: %s", hipGetErrorString(e));
     g_last_error[0] = '\0';

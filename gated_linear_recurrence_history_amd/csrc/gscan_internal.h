@@ -42,11 +42,24 @@ hipError_t launch_forward(const Plan &p, const void *h_history, const void *h_s2
                           const float *W_A, const float *W_B, const float *W_C,
                           float a_shift, float *context, hipStream_t stream);
 
-// Phase 1: per-workgroup weight-gradient partials into `partials`.
+// Phase 1: per-workgroup weight-gradient partials into `partials`.  When
+// `dab` / `dc` are not null they receive, for the input gradients, either
+// the final dL/dA | dL/dB per row ([B*K][2D]) and dL/dC per sample ([B][D])
+// (p.bwd_rows_kernel), or the projections A | Bv and C in the same places,
+// which launch_adjoint then turns into those adjoints.
 hipError_t launch_backward_partials(const Plan &p, const void *h_history, const void *h_s2,
                                     const float *W_A, const float *W_B, const float *W_C,
                                     float a_shift, const float *d_context, float *partials,
-                                    hipStream_t stream);
+                                    float *dab, float *dc, hipStream_t stream);
+
+// In place: A | Bv -> dL/dA | dL/dB per row, C -> dL/dC per sample.
+hipError_t launch_adjoint(const Plan &p, float *ab, float *cv, const float *d_context,
+                          float a_shift, hipStream_t stream);
+
+// out[nrows][SH2] = in[nrows][KD] x [W1 | W2]^T (W1 [SH2][D1], W2 [SH2][KD-D1]).
+hipError_t launch_dinput(const float *in, const float *W1, const float *W2, int64_t D1,
+                         int64_t KD, int64_t SH2, int64_t nrows, float *out,
+                         hipStream_t stream);
 
 // Phase 2: fixed-order sum of the partials into dW_A, dW_B, dW_C.
 hipError_t launch_backward_reduce(const Plan &p, const float *partials, float *dW_A,

@@ -730,7 +730,8 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                  const float *__restrict__ WA, const float *__restrict__ WB,
                  const float *__restrict__ WC, int64_t B, int K, int D, int slices,
                  int64_t groups, int64_t nrows, float a_shift, const float *__restrict__ dctx,
-                 float *__restrict__ part)
+                 float *__restrict__ part, float *__restrict__ ab_out,
+                 float *__restrict__ cv_out)
 {
     constexpr int SH2 = NQ * 32;
     constexpr int NSB = nsb_of(NQ);
@@ -822,6 +823,12 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             for (int j = 0; j < 4; ++j) cvp[gpar][wave][4 * kg + j][ln] = cp[j];
         }
         __syncthreads();
+        if (cv_out) {  // C of the group's samples, for the input gradients
+            const int bl = tid >> 4, s = tid & 15;
+            if (bl < nb)
+                cv_out[(b0 + bl) * D + s0 + s] = cvp[gpar][0][bl][s] + cvp[gpar][1][bl][s] +
+                                                 cvp[gpar][2][bl][s] + cvp[gpar][3][bl][s];
+        }
         // lambda_K = dL/dx_K = d_context * C for local sample bl, state l%16
         auto lam = [&](int bl) {
             return dctl[gpar][bl][ln] * (cvp[gpar][0][bl][ln] + cvp[gpar][1][bl][ln] +
@@ -847,6 +854,23 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             {
                 const PBlk<TIn, NQ> one[1] = {pb};
                 project<TIn, NQ, 1>(one, Wl, lane, aA, aB);
+            }
+            if (ab_out) {
+                // the projections A | Bv of this block's rows, for the input
+                // gradients (samples may continue past the chunk, so the
+                // exact adjoints come from a later per-sample pass).  Lane
+                // indices from an opaque zero, computed here, not held.
+                int z;
+                asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+                const int zl = (threadIdx.x + z) & 63;
+                const int zr = cb + kBlockRows * wave + 4 * (zl >> 4);
+                float *o = ab_out + (b0 * K + zr) * (int64_t)(2 * D) + s0 + (zl & 15);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (zr + j < ce) {
+                        o[j * 2 * D] = aA[0][j];
+                        o[j * 2 * D + D] = aB[0][j];
+                    }
             }
 
             // per-row maps (forward state and reverse adjoint)
@@ -1129,7 +1153,8 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                       const float *__restrict__ WA, const float *__restrict__ WB,
                       const float *__restrict__ WC, int64_t B, int K, int D, int slices,
                       int64_t groups, int64_t nrows, float a_shift,
-                      const float *__restrict__ dctx, float *__restrict__ part)
+                      const float *__restrict__ dctx, float *__restrict__ part,
+                      float *__restrict__ dab_out, float *__restrict__ dc_out)
 {
     constexpr int SH2 = NQ * 32;
     constexpr int NH = NQ / 2;        // units per column half
@@ -1401,6 +1426,16 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             if (j > 0) m_in = tj[j] == 0 ? lprev[j] : gt * m_in;
         }
 
+        if (dab_out && half == 0) {
+            // dL/dA | dL/dB of this block's rows, for the input gradients
+            float *o = dab_out + (cur.g * kGroupSamples * K + lr0 + 4 * kg) * (int64_t)(2 * D) + s0 + ln;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (lr0 + 4 * kg + j < ce) {
+                    o[j * 2 * D] = dA4[j];
+                    o[j * 2 * D + D] = dB4[j];
+                }
+        }
         // weight-gradient contraction of this half over the block's 16 rows
         const GradOp gA = grad_op<LO>(dA4), gB = grad_op<LO>(dB4);
         const uint16_t *const trp = tile + (4 * kg + (ln >> 2)) * kPitch + 4 * (ln & 3);
@@ -1421,6 +1456,10 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 
         if (c == nch - 1) {
             __syncthreads();  // dL/dC of the whole group written
+            if (dc_out && tid < 256) {
+                const int bl = tid >> 4, s = tid & 15;
+                if (bl < nb) dc_out[(cur.g * kGroupSamples + bl) * D + s0 + s] = dCl[bl][s];
+            }
             // dW_C of unit `wave` over the group's samples (k = sample), the
             // split unit read back transposed
             f4 dc;
@@ -1557,6 +1596,116 @@ gscan_reduce_kernel(const float *__restrict__ part, int64_t nrows, int64_t wsz,
     }
 }
 
+// Exact adjoints per (sample, state) from stored projections, in place:
+// ab [B*K][2D] holds A | Bv on entry and dL/dA | dL/dB on exit; cv [B][D]
+// holds C on entry and dL/dC on exit.  The forward pass keeps x_t in the Bv
+// slot (Bv_t is not needed once x_{t+1} is known); the reverse pass reads A_t
+// and x_t and overwrites both slots.  Used where samples cross the backward
+// kernel's chunks (its per-row adjoints there are provisional).
+__global__ void __launch_bounds__(kThreads)
+gscan_adjoint_kernel(float *__restrict__ ab, float *__restrict__ cv,
+                     const float *__restrict__ dctx, int64_t B, int64_t K, int D, float a_shift)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= B * D) return;
+    const int64_t b = i / D;
+    const int s = (int)(i - b * D);
+    float *base = ab + b * K * 2 * D + s;
+    float x = 0.f;
+    for (int64_t t = 0; t < K; ++t) {
+        float *row = base + t * 2 * D;
+        const float g = sigmoid(row[0] + a_shift);
+        const float bv = row[D];
+        row[D] = x;  // x_t
+        x = g * x + bv;
+    }
+    const float d = dctx[i];
+    float lam = d * cv[i];
+    cv[i] = d * x;  // dL/dC = d_context * x_K
+    for (int64_t t = K - 1; t >= 0; --t) {
+        float *row = base + t * 2 * D;
+        const float g = sigmoid(row[0] + a_shift);
+        const float xt = row[D];
+        row[D] = lam;                      // dL/dBv_t
+        row[0] = lam * xt * (g * (1.f - g));  // dL/dA_t
+        lam = g * lam;
+    }
+}
+
+// ===================================================== input gradients
+// out[r][i] = sum_k in[r][k] * Wk(k, i) over k < KD, where Wk(k, i) is
+// W1[i][k] for k < D1 and W2[i][k - D1] otherwise: d_h_history from
+// [dL/dA | dL/dB] rows (W1 = W_A, W2 = W_B, KD = 2D) and d_h_s2 from dL/dC rows
+// (W1 = W_C, KD = D).  Computed transposed on the matrix cores, outᵀ tile =
+// Wkᵀ tile x inᵀ tile, so a lane ends with four consecutive columns of one
+// row (one 128-bit store).  Both operands fp32, split hi/lo (3 bf16 MFMA per
+// product).  A workgroup stages the split weights of CT column tiles for all
+// k (zero past KD) in LDS, then walks 64-row tiles (16 rows per wavefront).
+constexpr int kDinRows = 64;
+
+template <int CT>
+__global__ void __launch_bounds__(kThreads)
+gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
+                    const float *__restrict__ W2, int D1, int KD, int SH2, int64_t nrows,
+                    float *__restrict__ out)
+{
+    extern __shared__ u4 img[];  // [kc][ct][hi, lo][lane]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kg = lane >> 4, ln = lane & 15;
+    const int nkc = (KD + 31) / 32;
+    const int c0 = blockIdx.y * CT * 16;
+    for (int e0 = tid; e0 < nkc * CT * kWave; e0 += kThreads) {
+        const int l = e0 & (kWave - 1), ct = (e0 / kWave) % CT, kc = e0 / kWave / CT;
+        const int i = c0 + 16 * ct + (l & 15);
+        const int k = 32 * kc + 8 * (l >> 4);  // eight k on one side of D1 (D1 % 16 == 0)
+        float v[8];
+        if (k < KD) {
+            const float *src = k < D1 ? W1 + (int64_t)i * D1 + k
+                                      : W2 + (int64_t)i * (KD - D1) + (k - D1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = src[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+        const Split sp = split8(v);
+        img[((kc * CT + ct) * 2 + 0) * kWave + l] = sp.hi;
+        img[((kc * CT + ct) * 2 + 1) * kWave + l] = sp.lo;
+    }
+    __syncthreads();
+    const int64_t tiles = (nrows + kDinRows - 1) / kDinRows;
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int64_t r = t * kDinRows + 16 * wave + ln;
+        const float *rowp = in + (r < nrows ? r : nrows - 1) * (int64_t)KD;
+        f4 acc[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = zero4();
+        for (int kc = 0; kc < nkc; ++kc) {
+            const int k = 32 * kc + 8 * kg;
+            const bool kin = k < KD;
+            const float *src = rowp + (kin ? k : 0);
+            const f4 a = *reinterpret_cast<const f4 *>(src);
+            const f4 b = *reinterpret_cast<const f4 *>(src + 4);
+            float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = kin ? x[e] : 0.f;
+            const Split hs = split8(x);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                Split w;
+                w.hi = img[((kc * CT + ct) * 2 + 0) * kWave + lane];
+                w.lo = img[((kc * CT + ct) * 2 + 1) * kWave + lane];
+                acc[ct] = mfma3<true>(w, hs, acc[ct]);
+            }
+        }
+        if (r < nrows) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                *reinterpret_cast<f4 *>(out + r * SH2 + c0 + 16 * ct + 4 * kg) = acc[ct];
+        }
+    }
+}
+
 // ----------------------------------------------------------------- dispatch
 template <typename TIn, int NQ>
 hipError_t fwd_launch(const Plan &p, const void *hh, const void *hs2, const float *WA,
@@ -1572,7 +1721,7 @@ hipError_t fwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
 template <typename TIn, int NQ>
 hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const float *WA,
                       const float *WB, const float *WC, float a_shift, const float *dctx,
-                      float *part, hipStream_t st)
+                      float *part, float *dab, float *dc, hipStream_t st)
 {
     const bool aligned = 16 % p.K == 0;
     if constexpr (NQ <= 8) {
@@ -1580,7 +1729,7 @@ hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
             hipLaunchKernelGGL((gscan_bwd_rows_kernel<TIn, NQ>), dim3((unsigned)p.bwd_grid),
                                dim3(kThreads2), 0, st, static_cast<const TIn *>(hh),
                                static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
-                               p.slices, p.groups, p.bwd_rows, a_shift, dctx, part);
+                               p.slices, p.groups, p.bwd_rows, a_shift, dctx, part, dab, dc);
             return hipGetLastError();
         }
     }
@@ -1588,12 +1737,12 @@ hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
         hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ, true>), dim3((unsigned)p.bwd_grid),
                            dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
                            static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
-                           p.slices, p.groups, p.bwd_rows, a_shift, dctx, part);
+                           p.slices, p.groups, p.bwd_rows, a_shift, dctx, part, dab, dc);
     else
         hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ, false>), dim3((unsigned)p.bwd_grid),
                            dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
                            static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
-                           p.slices, p.groups, p.bwd_rows, a_shift, dctx, part);
+                           p.slices, p.groups, p.bwd_rows, a_shift, dctx, part, dab, dc);
     return hipGetLastError();
 }
 
@@ -1617,17 +1766,17 @@ hipError_t fwd_by_nq(const Plan &p, const void *hh, const void *hs2, const float
 template <typename TIn>
 hipError_t bwd_by_nq(const Plan &p, const void *hh, const void *hs2, const float *WA,
                      const float *WB, const float *WC, float a, const float *dctx, float *part,
-                     hipStream_t st)
+                     float *dab, float *dc, hipStream_t st)
 {
     switch (p.nq) {
-    case 2: return bwd_launch<TIn, 2>(p, hh, hs2, WA, WB, WC, a, dctx, part, st);
-    case 4: return bwd_launch<TIn, 4>(p, hh, hs2, WA, WB, WC, a, dctx, part, st);
-    case 6: return bwd_launch<TIn, 6>(p, hh, hs2, WA, WB, WC, a, dctx, part, st);
-    case 8: return bwd_launch<TIn, 8>(p, hh, hs2, WA, WB, WC, a, dctx, part, st);
-    case 10: return bwd_launch<TIn, 10>(p, hh, hs2, WA, WB, WC, a, dctx, part, st);
-    case 12: return bwd_launch<TIn, 12>(p, hh, hs2, WA, WB, WC, a, dctx, part, st);
-    case 14: return bwd_launch<TIn, 14>(p, hh, hs2, WA, WB, WC, a, dctx, part, st);
-    case 16: return bwd_launch<TIn, 16>(p, hh, hs2, WA, WB, WC, a, dctx, part, st);
+    case 2: return bwd_launch<TIn, 2>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
+    case 4: return bwd_launch<TIn, 4>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
+    case 6: return bwd_launch<TIn, 6>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
+    case 8: return bwd_launch<TIn, 8>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
+    case 10: return bwd_launch<TIn, 10>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
+    case 12: return bwd_launch<TIn, 12>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
+    case 14: return bwd_launch<TIn, 14>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
+    case 16: return bwd_launch<TIn, 16>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1680,10 +1829,44 @@ hipError_t launch_forward(const Plan &p, const void *hh, const void *hs2, const 
 
 hipError_t launch_backward_partials(const Plan &p, const void *hh, const void *hs2,
                                     const float *WA, const float *WB, const float *WC,
-                                    float a_shift, const float *dctx, float *part, hipStream_t st)
+                                    float a_shift, const float *dctx, float *part, float *dab,
+                                    float *dc, hipStream_t st)
 {
-    return p.dtype == 1 ? bwd_by_nq<uint16_t>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, st)
-                        : bwd_by_nq<float>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, st);
+    return p.dtype == 1
+               ? bwd_by_nq<uint16_t>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, st)
+               : bwd_by_nq<float>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, st);
+}
+
+hipError_t launch_adjoint(const Plan &p, float *ab, float *cv, const float *dctx, float a_shift,
+                          hipStream_t st)
+{
+    const int64_t n = p.B * p.D;
+    hipLaunchKernelGGL(gscan_adjoint_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, st, ab, cv, dctx, p.B, p.K, (int)p.D, a_shift);
+    return hipGetLastError();
+}
+
+hipError_t launch_dinput(const float *in, const float *W1, const float *W2, int64_t D1, int64_t KD,
+                         int64_t SH2, int64_t nrows, float *out, hipStream_t st)
+{
+    if (nrows <= 0) return hipSuccess;
+    const int nkc = (int)((KD + 31) / 32);
+    const int tiles16 = (int)(SH2 / 16);
+    int ct = 16;
+    while (ct > 1 && (ct * nkc > 32 || tiles16 % ct != 0)) ct /= 2;
+    const size_t shmem = (size_t)nkc * ct * 2 * kWave * sizeof(u4);
+    const int64_t row_tiles = (nrows + kDinRows - 1) / kDinRows;
+    const unsigned gx = (unsigned)(row_tiles < 512 ? row_tiles : 512);
+    const dim3 grid(gx, (unsigned)(tiles16 / ct));
+    const int d1 = (int)D1, kd = (int)KD, sh2 = (int)SH2;
+    switch (ct) {
+    case 16: hipLaunchKernelGGL(gscan_dinput_kernel<16>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    case 8: hipLaunchKernelGGL(gscan_dinput_kernel<8>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    case 4: hipLaunchKernelGGL(gscan_dinput_kernel<4>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    case 2: hipLaunchKernelGGL(gscan_dinput_kernel<2>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    default: hipLaunchKernelGGL(gscan_dinput_kernel<1>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_backward_reduce(const Plan &p, const float *part, float *dWA, float *dWB,

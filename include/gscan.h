@@ -138,6 +138,33 @@ int gscan_backward_reduce(const void *workspace, size_t workspace_bytes,
                           gscan_dtype_t in_dtype, float *dW_A, float *dW_B, float *dW_C,
                           hipStream_t stream);
 
+/*
+ * Backward with input gradients: everything gscan_backward_ex computes, and
+ * the gradients of L with respect to the inputs, by the chain rule through
+ * the three projections of Forward Step 1:
+ *   d_h_history[b*K+t][i] = sum_s dL/dA_vals[b*K+t][s] W_A[i][s]
+ *                                + dL/dB_vals[b*K+t][s] W_B[i][s]
+ *   d_h_s2[b][i]          = sum_s dL/dC_vals[b][s] W_C[i][s]
+ * (the design spec's backward stops at the weight gradients; these are what
+ * a layer below the scan needs).  d_h_history [B*K][SH2] and d_h_s2 [B][SH2]
+ * are fp32 row-major for either input dtype, caller-owned, 16-byte aligned,
+ * overwritten.  workspace: at least gscan_backward_full_workspace_bytes(),
+ * 256-byte aligned, or NULL to allocate stream-ordered; it holds the
+ * weight-gradient partials, dL/dA | dL/dB per row and dL/dC per sample;
+ * contents on entry are ignored.  Errors as for gscan_backward_ex.
+ */
+int gscan_backward_full_ex(const void *h_history, const void *h_s2,
+                           const float *W_A, const float *W_B, const float *W_C,
+                           int64_t B, int64_t K, int64_t SH2, int64_t D,
+                           const float *d_context, float *dW_A, float *dW_B, float *dW_C,
+                           float *d_h_history, float *d_h_s2,
+                           gscan_dtype_t in_dtype, float a_shift,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes gscan_backward_full_ex needs for this shape (0 if unsupported). */
+size_t gscan_backward_full_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
+                                           gscan_dtype_t in_dtype);
+
 /* Workspace bytes gscan_backward_ex needs for this shape (0 if unsupported). */
 size_t gscan_backward_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
                                       gscan_dtype_t in_dtype);

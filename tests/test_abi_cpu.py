@@ -104,3 +104,32 @@ def test_plain_entry_points_validate(lib):
     assert lib.gscan_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 8, 256, 12, FAKE, FAKE, FAKE,
                               FAKE, None) == UNSUPPORTED
     assert b"unsupported shape" in lib.gscan_last_error()
+
+
+def _bfull(lib, B=64, K=8, SH2=256, D=16, dctx=FAKE, dwa=FAKE, dh=FAKE, dhs=FAKE, ws=None,
+           ws_bytes=0, dtype=0, hh=FAKE):
+    return lib.gscan_backward_full_ex(hh, FAKE, FAKE, FAKE, FAKE, B, K, SH2, D, dctx, dwa, FAKE,
+                                      FAKE, dh, dhs, dtype, 0.0, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dctx=None), INVALID), (dict(dwa=None), INVALID), (dict(dh=None), INVALID),
+    (dict(dhs=None), INVALID), (dict(hh=None), INVALID), (dict(D=17), UNSUPPORTED),
+    (dict(dh=FAKE + 4), MISALIGNED), (dict(dhs=FAKE + 8), MISALIGNED),
+    (dict(ws=FAKE, ws_bytes=16), WS_SMALL),
+    (dict(ws=FAKE + 16, ws_bytes=1 << 40), MISALIGNED),
+])
+def test_backward_full_validation(lib, kw, code):
+    assert _bfull(lib, **kw) == code
+    assert lib.gscan_last_error() != b""
+
+
+def test_backward_full_workspace_bytes(lib):
+    # partials, then dL/dA | dL/dB per row and dL/dC per sample
+    for cfg in wl.WORKLOADS:
+        dt = 1 if cfg.in_dtype == "bf16" else 0
+        part = lib.gscan_backward_workspace_bytes(cfg.B, cfg.K, cfg.SH2, cfg.D, dt)
+        full = lib.gscan_backward_full_workspace_bytes(cfg.B, cfg.K, cfg.SH2, cfg.D, dt)
+        extra = 4 * (cfg.B * cfg.K * 2 * cfg.D + cfg.B * cfg.D)
+        assert part + extra <= full <= part + extra + 512
+    assert lib.gscan_backward_full_workspace_bytes(64, 8, 100, 16, 0) == 0

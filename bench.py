@@ -19,6 +19,12 @@ Fields beyond the headline value:
                     (profiles/traffic_<kernel>_<workload>.txt), else null
   cpu_baseline      the fp64 CPU oracle timed on a bounded sample of the
                     same workload on this host's cores
+  input_grads       the backward that also returns the input gradients
+                    (gscan_backward_full_ex): HIP-event time per call on the
+                    same rotated inputs, its algorithmic bytes (the backward's
+                    plus d_h_history and d_h_s2 written) against 8 TB/s, the
+                    time over the plain backward, and the oracle's rate for
+                    the input gradients on a small sample
 
 The matrix products run on bf16 MFMA with fp32 operands split into a high
 and a low bf16 part (three products per fp32 product), so the MFMA time of a
@@ -51,6 +57,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-input-grads", action="store_true",
+                    help="skip the timing of the backward with input gradients")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finish with 4 untimed device copies of this many MiB (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -90,6 +98,59 @@ def cpu_baseline(w, target_s):
             "kind": "oracle",
             "sample": f"first {n} of {w.B} samples of {w.name}, fp64 forward+backward, "
                       f"{reps} passes in {t:.1f} s"}
+
+
+def input_grads(args, w, sets, stream, bwd_us, reps):
+    """gscan_backward_full_ex per call (HIP events, rotated inputs) and the
+    oracle's input-gradient rate on a small sample."""
+    import torch
+
+    import oracle
+    from gated_linear_recurrence_history_amd import binding, synth
+
+    dev = sets[0]["h_history"].device
+    bf = w.in_dtype == "bf16"
+    out = tuple(torch.empty((w.SH2, w.D), device=dev) for _ in range(3)) + (
+        torch.empty((w.rows, w.SH2), device=dev), torch.empty((w.B, w.SH2), device=dev))
+    ws = torch.empty(binding.backward_full_workspace_bytes(w.B, w.K, w.SH2, w.D, bf),
+                     dtype=torch.uint8, device=dev)
+    fns = [binding.prepare_backward_full(t["h_history"], t["h_s2"], t["W_A"], t["W_B"],
+                                         t["W_C"], w.K, t["d_context"], out, ws, w.a_shift,
+                                         stream) for t in sets]
+    n = len(fns)
+    for i in range(max(args.warmup, n)):
+        fns[i % n]()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(reps):
+        fns[i % n]()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    nbytes = w.bwd_bytes() + w.dinput_out_bytes()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    # oracle on the first samples (at most 256), about a second of work
+    ns = min(w.B, 256)
+    x = synth.make_inputs(w, B=ns)
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.backward_inputs(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], w.K,
+                               x["d_context"], w.a_shift)
+        passes += 1
+        if time.perf_counter() - t0 > 1.0:
+            break
+    t = time.perf_counter() - t0
+    return {"entry": "gscan_backward_full_ex", "us_per_call": round(us, 3),
+            "samples_per_s": round(w.B / (us * 1e-6), 1), "algorithmic_bytes": nbytes,
+            "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "over_backward_us": round(us - bwd_us, 3),
+            "oracle": {"value": round(ns * passes / t, 1), "unit": "samples/s",
+                       "cores": oracle.max_threads(),
+                       "sample": f"first {ns} samples, fp64 input gradients, {passes} passes "
+                                 f"in {t:.1f} s"}}
 
 
 def traffic_record(kernel, workload):
@@ -231,6 +292,8 @@ def main():
                        "gscan_reduce_kernel": round(k_red, 3)},
         "roofline": roof,
     }
+    if not args.no_input_grads:
+        out["input_grads"] = input_grads(args, w, sets, stream, k_bwd + k_red, reps)
     if args.copy_calibration_mib > 0:
         nb = args.copy_calibration_mib << 20
         src = torch.ones(nb, dtype=torch.uint8, device=dev)

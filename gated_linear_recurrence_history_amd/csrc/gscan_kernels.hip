@@ -1642,8 +1642,10 @@ gscan_adjoint_kernel(float *__restrict__ ab, float *__restrict__ cv,
 // product).  A workgroup stages the split weights of CT column tiles for all
 // k (zero past KD) in LDS, then walks 64-row tiles (16 rows per wavefront).
 constexpr int kDinRows = 64;
+constexpr int64_t kDinMaxRowBlocks = 1024;  // persistent row blocks per column slice
 
-template <int CT>
+// WHICH only names the launch in profiles: 0 for d_h_history, 1 for d_h_s2
+template <int CT, int WHICH>
 __global__ void __launch_bounds__(kThreads)
 gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
                     const float *__restrict__ W2, int D1, int KD, int SH2, int64_t nrows,
@@ -1846,27 +1848,38 @@ hipError_t launch_adjoint(const Plan &p, float *ab, float *cv, const float *dctx
     return hipGetLastError();
 }
 
-hipError_t launch_dinput(const float *in, const float *W1, const float *W2, int64_t D1, int64_t KD,
-                         int64_t SH2, int64_t nrows, float *out, hipStream_t st)
+template <int WHICH>
+hipError_t launch_dinput_which(const float *in, const float *W1, const float *W2, int64_t D1,
+                               int64_t KD, int64_t SH2, int64_t nrows, float *out, hipStream_t st)
 {
     if (nrows <= 0) return hipSuccess;
     const int nkc = (int)((KD + 31) / 32);
     const int tiles16 = (int)(SH2 / 16);
-    int ct = 16;
-    while (ct > 1 && (ct * nkc > 32 || tiles16 % ct != 0)) ct /= 2;
-    const size_t shmem = (size_t)nkc * ct * 2 * kWave * sizeof(u4);
     const int64_t row_tiles = (nrows + kDinRows - 1) / kDinRows;
-    const unsigned gx = (unsigned)(row_tiles < 512 ? row_tiles : 512);
+    // widest column slice whose weight image fits (<= 64 KiB), narrowed
+    // while there are too few (row tile, slice) pairs to fill the chip
+    int ct = 16;
+    while (ct > 1 && (ct * nkc > 32 || tiles16 % ct != 0 || row_tiles * (tiles16 / ct) < 1024))
+        ct /= 2;
+    const size_t shmem = (size_t)nkc * ct * 2 * kWave * sizeof(u4);
+    const unsigned gx = (unsigned)(row_tiles < kDinMaxRowBlocks ? row_tiles : kDinMaxRowBlocks);
     const dim3 grid(gx, (unsigned)(tiles16 / ct));
     const int d1 = (int)D1, kd = (int)KD, sh2 = (int)SH2;
     switch (ct) {
-    case 16: hipLaunchKernelGGL(gscan_dinput_kernel<16>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
-    case 8: hipLaunchKernelGGL(gscan_dinput_kernel<8>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
-    case 4: hipLaunchKernelGGL(gscan_dinput_kernel<4>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
-    case 2: hipLaunchKernelGGL(gscan_dinput_kernel<2>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
-    default: hipLaunchKernelGGL(gscan_dinput_kernel<1>, grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    case 16: hipLaunchKernelGGL((gscan_dinput_kernel<16, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    case 8: hipLaunchKernelGGL((gscan_dinput_kernel<8, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    case 4: hipLaunchKernelGGL((gscan_dinput_kernel<4, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    case 2: hipLaunchKernelGGL((gscan_dinput_kernel<2, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
+    default: hipLaunchKernelGGL((gscan_dinput_kernel<1, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_dinput(const float *in, const float *W1, const float *W2, int64_t D1, int64_t KD,
+                         int64_t SH2, int64_t nrows, float *out, hipStream_t st)
+{
+    return W2 ? launch_dinput_which<0>(in, W1, W2, D1, KD, SH2, nrows, out, st)
+              : launch_dinput_which<1>(in, W1, W2, D1, KD, SH2, nrows, out, st);
 }
 
 hipError_t launch_backward_reduce(const Plan &p, const float *part, float *dWA, float *dWB,

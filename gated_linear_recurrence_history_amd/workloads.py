@@ -63,6 +63,10 @@ class Workload:
                 + 3 * self.SH2 * self.D * 4 + self.B * self.D * 4
                 + 3 * self.SH2 * self.D * 4)
 
+    def dinput_out_bytes(self) -> int:
+        """The input gradients written: d_h_history [B*K][SH2], d_h_s2 [B][SH2], fp32."""
+        return self.rows * self.SH2 * 4 + self.B * self.SH2 * 4
+
     # --- algorithmic multiply-add work (2 FLOP per MAC), scan terms ignored
     def fwd_flops(self) -> int:
         return 2 * self.rows * self.SH2 * 2 * self.D + 2 * self.B * self.SH2 * self.D

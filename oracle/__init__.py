@@ -4,7 +4,7 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
 import this package.  The product path (the HIP library and its binding)
 never touches it.
 
-`forward` / `backward` / `backward_inputs` widen every input exactly to float64 (float32 as is,
+`forward` / `backward` / `backward_inputs` / `column_sums` widen every input exactly to float64 (float32 as is,
 bfloat16 given as raw uint16 bits by zero-extending the low mantissa) and
 call plain double-precision C loops (gscan_oracle.c).
 """
@@ -38,6 +38,8 @@ def _load():
         lib.oracle_backward_inputs.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
                                                ctypes.c_double, dp, dp, dp]
         lib.oracle_backward_inputs.restype = None
+        lib.oracle_column_sums.argtypes = [dp, i64, i64, dp]
+        lib.oracle_column_sums.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -108,6 +110,18 @@ def backward_inputs(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: 
                                    wb.ctypes.data, wc.ctypes.data, B, K, SH2, D, float(a_shift),
                                    dc.ctypes.data, dh.ctypes.data, dhs.ctypes.data)
     return dh, dhs
+
+
+def column_sums(grad) -> np.ndarray:
+    """out[j] = sum_r grad[r, j] in float64 (the bias-gradient reduction)."""
+    g = widen(grad)
+    if g.ndim != 2:
+        raise ValueError(f"grad must be 2-D, got shape {g.shape}")
+    g = np.ascontiguousarray(g)
+    rows, cols = g.shape
+    out = np.empty(cols, dtype=np.float64)
+    _load().oracle_column_sums(g.ctypes.data, rows, cols, out.ctypes.data)
+    return out
 
 
 def sample_rows(inputs: dict, K: int, samples) -> dict:

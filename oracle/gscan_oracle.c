@@ -302,3 +302,23 @@ void oracle_backward_inputs(const double *h_history, const double *h_s2,
         free(dC);
     }
 }
+
+/*
+ * Batch-parallel bias-gradient reduction (design spec section "IQN Bias
+ * Grad Reduce", and the KAN / Q-denoise bias gradients that follow its
+ * pattern): out[j] = sum over rows r of grad[r, j], for a row-major
+ * [rows, cols] gradient.  The plain definition: one running fp64 sum per
+ * column, rows in order.
+ */
+void oracle_column_sums(const double *grad, int64_t rows, int64_t cols, double *out)
+{
+    int64_t j;
+#pragma omp parallel for schedule(static)
+    for (j = 0; j < cols; ++j) {
+        double acc = 0.0;
+        int64_t r;
+        for (r = 0; r < rows; ++r)
+            acc += grad[r * cols + j];
+        out[j] = acc;
+    }
+}

@@ -49,6 +49,12 @@ MUTANTS = {
                               "dC[s] = d_context[b * D + s];"),
     "dhs2_wrong_weight": ("v += dC[s] * W_C[ii * D + s];", "v += dC[s] * W_B[ii * D + s];"),
     "dh_a_shift_ignored": ("sigmoid(a_shift + Av[s]);", "sigmoid(Av[s]);"),
+    # bias-gradient reduction
+    "colsum_transposed": ("acc += grad[r * cols + j];", "acc += grad[j * rows + r];"),
+    "colsum_drops_last_row": ("for (r = 0; r < rows; ++r)\n            acc",
+                              "for (r = 0; r + 1 < rows; ++r)\n            acc"),
+    "colsum_shifted_column": ("acc += grad[r * cols + j];",
+                              "acc += grad[r * cols + (j + 1) % cols];"),
 }
 
 
@@ -65,6 +71,8 @@ def _pins():
     yield lambda: pins.test_input_grad_k1_and_linearity()
     for a in (-3.0, 0.0, 2.0):
         yield lambda a=a: pins.test_input_grad_central_finite_differences(a)
+    yield pins.test_column_sums_exact_cases
+    yield pins.test_column_sums_against_correctly_rounded_sums
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -79,8 +87,8 @@ def test_mutant_is_caught(name, tmp_path):
                     str(lib_path), "-lm"], check=True)
     real = oracle._load()
     mut = ctypes.CDLL(str(lib_path))
-    for fn in ("oracle_forward", "oracle_backward", "oracle_backward_inputs", "oracle_max_threads",
-               "oracle_set_threads"):
+    for fn in ("oracle_forward", "oracle_backward", "oracle_backward_inputs", "oracle_column_sums",
+               "oracle_max_threads", "oracle_set_threads"):
         getattr(mut, fn).argtypes = getattr(real, fn).argtypes
         getattr(mut, fn).restype = getattr(real, fn).restype
     caught = False

@@ -281,3 +281,29 @@ def test_input_grad_k1_and_linearity():
     g12 = _bin(y, K, -0.5, d1 - 3.0 * d2)
     for a, b, c in zip(g1, g2, g12):
         assert _rel(c, a - 3.0 * b) < 1e-12
+
+
+# ------------------------------------------------ bias-gradient reduction
+def test_column_sums_exact_cases():
+    # integers (exact in fp64 at this size), a constant column, an empty batch
+    rng = np.random.default_rng(31)
+    g = rng.integers(-1000, 1000, size=(5000, 7)).astype(np.float64)
+    assert np.array_equal(oracle.column_sums(g), g.sum(axis=0, dtype=np.int64).astype(np.float64))
+    c = np.full((1234, 3), 0.75)
+    assert np.array_equal(oracle.column_sums(c), np.full(3, 1234 * 0.75))
+    assert np.array_equal(oracle.column_sums(np.zeros((0, 4))), np.zeros(4))
+
+
+def test_column_sums_against_correctly_rounded_sums():
+    # math.fsum is the correctly rounded sum: the plain fp64 running sum of
+    # n float32 values stays within n * 2^-53 * sum|x| of it
+    rng = np.random.default_rng(32)
+    g = rng.standard_normal((20000, 3)).astype(np.float32)
+    got = oracle.column_sums(g)
+    for j in range(3):
+        col = g[:, j].astype(np.float64)
+        exact = math.fsum(col.tolist())
+        assert abs(got[j] - exact) <= len(col) * 2.0 ** -53 * np.abs(col).sum()
+    # columns are not mixed: permuting columns permutes the result
+    perm = [2, 0, 1]
+    assert np.array_equal(oracle.column_sums(np.ascontiguousarray(g[:, perm])), got[perm])

@@ -62,6 +62,10 @@ def lib():
         L.gscan_backward_full_ex.restype = ctypes.c_int
         L.gscan_backward_full_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.gscan_backward_full_workspace_bytes.restype = ctypes.c_size_t
+        L.gscan_bias_grad_reduce.argtypes = [vp, i64, i64, vp, vp, ctypes.c_size_t, vp]
+        L.gscan_bias_grad_reduce.restype = ctypes.c_int
+        L.gscan_bias_grad_reduce_workspace_bytes.argtypes = [i64, i64]
+        L.gscan_bias_grad_reduce_workspace_bytes.restype = ctypes.c_size_t
         L.gscan_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.gscan_backward_workspace_bytes.restype = ctypes.c_size_t
         L.gscan_status_string.argtypes = [ctypes.c_int]
@@ -210,6 +214,32 @@ def prepare_backward_full(h_history, h_s2, W_A, W_B, W_C, K, d_context, out, wor
             _stream_handle(stream, dev))
     return Prepared(lib().gscan_backward_full_ex, args,
                     (h_history, h_s2, W_A, W_B, W_C, d_context, out, workspace))
+
+
+def bias_grad_reduce(grad, out=None, workspace=None, stream=None):
+    """out[j] = sum_r grad[r, j] (float32 [cols]) for a contiguous float32
+    [rows, cols] GPU tensor: the batch-parallel bias-gradient reduction."""
+    import torch
+    if (not grad.is_cuda or grad.dtype != torch.float32 or grad.dim() != 2
+            or not grad.is_contiguous()):
+        raise ValueError("grad must be a contiguous float32 [rows, cols] GPU tensor")
+    rows, cols = grad.shape
+    if out is None:
+        out = torch.empty(cols, dtype=torch.float32, device=grad.device)
+    if workspace is None:
+        n = int(lib().gscan_bias_grad_reduce_workspace_bytes(rows, cols))
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=grad.device)
+    _check(lib().gscan_bias_grad_reduce(grad.data_ptr() if rows else None, rows, cols,
+                                        out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                        _stream_handle(stream, grad.device)))
+    return out
+
+
+def prepare_bias_grad_reduce(grad, out, workspace, stream=None):
+    rows, cols = grad.shape
+    args = (grad.data_ptr(), rows, cols, out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+            _stream_handle(stream, grad.device))
+    return Prepared(lib().gscan_bias_grad_reduce, args, (grad, out, workspace))
 
 
 def backward_partials(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, workspace,

@@ -234,6 +234,50 @@ int gscan_backward_full_ex(const void *h_history, const void *h_s2, const float 
     return GSCAN_OK;
 }
 
+size_t gscan_bias_grad_reduce_workspace_bytes(int64_t rows, int64_t cols)
+{
+    if (rows < 0 || cols < 1 || rows > (int64_t(1) << 40) / cols) return 0;
+    return gscan::colsum_workspace_bytes(rows, cols);
+}
+
+int gscan_bias_grad_reduce(const float *grad, int64_t rows, int64_t cols, float *out,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!out || (rows > 0 && !grad))
+        return fail(GSCAN_ERR_INVALID_ARGUMENT, "null pointer");
+    if (rows < 0 || cols < 1)
+        return fail(GSCAN_ERR_INVALID_ARGUMENT, "need rows >= 0 and cols >= 1 (rows=%lld cols=%lld)",
+                    (long long)rows, (long long)cols);
+    if (rows > (int64_t(1) << 40) / cols)
+        return fail(GSCAN_ERR_UNSUPPORTED_SHAPE, "rows x cols above 2^40");
+    if ((reinterpret_cast<uintptr_t>(grad) & 3u) != 0 || (reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+        return fail(GSCAN_ERR_MISALIGNED, "grad and out must be 4-byte aligned");
+    const size_t need = gscan::colsum_workspace_bytes(rows, cols);
+    if (workspace) {
+        if (workspace_bytes < need)
+            return fail(GSCAN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu",
+                        workspace_bytes, need);
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(GSCAN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    }
+    void *ws = workspace;
+    if (!ws) {
+        hipError_t e = hipMallocAsync(&ws, need, stream);
+        if (e != hipSuccess)
+            return fail(GSCAN_ERR_HIP, "workspace allocation of %zu bytes failed: %s", need,
+                        hipGetErrorString(e));
+    }
+    hipError_t e = gscan::launch_colsum(grad, rows, cols, out, ws, stream);
+    if (!workspace) {
+        hipError_t f = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = f;
+    }
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "bias-gradient reduction launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return GSCAN_OK;
+}
+
 int gscan_backward_partials(const void *h_history, const void *h_s2, const float *W_A,
                             const float *W_B, const float *W_C, int64_t B, int64_t K,
                             int64_t SH2, int64_t D, const float *d_context,

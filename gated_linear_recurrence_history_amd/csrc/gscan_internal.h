@@ -61,6 +61,12 @@ hipError_t launch_dinput(const float *in, const float *W1, const float *W2, int6
                          int64_t KD, int64_t SH2, int64_t nrows, float *out,
                          hipStream_t stream);
 
+// Bias-gradient reduction: out[j] = sum_r grad[r][j] (two phases, fp64
+// partials in `workspace` of colsum_workspace_bytes()).
+size_t colsum_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t launch_colsum(const float *grad, int64_t rows, int64_t cols, float *out,
+                         void *workspace, hipStream_t stream);
+
 // Phase 2: fixed-order sum of the partials into dW_A, dW_B, dW_C.
 hipError_t launch_backward_reduce(const Plan &p, const float *partials, float *dW_A,
                                   float *dW_B, float *dW_C, hipStream_t stream);

@@ -165,6 +165,25 @@ int gscan_backward_full_ex(const void *h_history, const void *h_s2,
 size_t gscan_backward_full_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
                                            gscan_dtype_t in_dtype);
 
+/*
+ * Batch-parallel bias-gradient reduction (design spec section "IQN Bias Grad
+ * Reduce"; the KAN and Q-denoise bias gradients share the pattern):
+ *   out[j] = sum over r < rows of grad[r][j],  j < cols
+ * grad: fp32 row-major [rows][cols] device memory (4-byte aligned; may be
+ * NULL when rows == 0), out: fp32 [cols], overwritten (zeros when rows == 0).
+ * Two phases with fp64 partials summed in a fixed order, so the result is
+ * bitwise reproducible.  workspace: at least
+ * gscan_bias_grad_reduce_workspace_bytes(rows, cols), 256-byte aligned, or
+ * NULL to allocate stream-ordered.  Errors: INVALID_ARGUMENT (null pointer,
+ * rows < 0, cols < 1), UNSUPPORTED_SHAPE (rows x cols above 2^40),
+ * MISALIGNED, WORKSPACE_TOO_SMALL, HIP_ERROR; nothing is launched on error.
+ */
+int gscan_bias_grad_reduce(const float *grad, int64_t rows, int64_t cols, float *out,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of gscan_bias_grad_reduce (0 for invalid sizes). */
+size_t gscan_bias_grad_reduce_workspace_bytes(int64_t rows, int64_t cols);
+
 /* Workspace bytes gscan_backward_ex needs for this shape (0 if unsupported). */
 size_t gscan_backward_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
                                       gscan_dtype_t in_dtype);

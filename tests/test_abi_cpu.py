@@ -133,3 +133,18 @@ def test_backward_full_workspace_bytes(lib):
         extra = 4 * (cfg.B * cfg.K * 2 * cfg.D + cfg.B * cfg.D)
         assert part + extra <= full <= part + extra + 512
     assert lib.gscan_backward_full_workspace_bytes(64, 8, 100, 16, 0) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 10, 3, FAKE), INVALID), ((FAKE, 10, 3, None), INVALID), ((FAKE, -1, 3, FAKE), INVALID),
+    ((FAKE, 10, 0, FAKE), INVALID), ((FAKE, 1 << 39, 4, FAKE), UNSUPPORTED),
+    ((FAKE + 2, 10, 3, FAKE), MISALIGNED),
+])
+def test_bias_grad_reduce_validation(lib, args, code):
+    assert lib.gscan_bias_grad_reduce(*args, None, 0, None) == code
+    assert lib.gscan_last_error() != b""
+    g, r, c, o = FAKE, 524288, 3, FAKE
+    n = lib.gscan_bias_grad_reduce_workspace_bytes(r, c)
+    assert n >= 8 * c
+    assert lib.gscan_bias_grad_reduce(g, r, c, o, FAKE, n - 8, None) == WS_SMALL
+    assert lib.gscan_bias_grad_reduce_workspace_bytes(10, 0) == 0

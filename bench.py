@@ -19,6 +19,10 @@ Fields beyond the headline value:
                     (profiles/traffic_<kernel>_<workload>.txt), else null
   cpu_baseline      the fp64 CPU oracle timed on a bounded sample of the
                     same workload on this host's cores
+  bias_grad_reduce  the batch-parallel bias-gradient reduction on the spec's
+                    IQN shape [524288 x 3] (fp32, synthetic N(0, 9)): HIP-event
+                    time per call, bytes read against 8 TB/s, and the
+                    oracle's rate
   input_grads       the backward that also returns the input gradients
                     (gscan_backward_full_ex): HIP-event time per call on the
                     same rotated inputs, its algorithmic bytes (the backward's
@@ -59,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-input-grads", action="store_true",
                     help="skip the timing of the backward with input gradients")
+    ap.add_argument("--no-bias-grad", action="store_true",
+                    help="skip the timing of the bias-gradient reduction")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finish with 4 untimed device copies of this many MiB (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -151,6 +157,51 @@ def input_grads(args, w, sets, stream, bwd_us, reps):
                        "cores": oracle.max_threads(),
                        "sample": f"first {ns} samples, fp64 input gradients, {passes} passes "
                                  f"in {t:.1f} s"}}
+
+
+def bias_grad(args, stream, reps, rows=524288, cols=3):
+    """gscan_bias_grad_reduce on the IQN shape: per call (HIP events) over
+    several distinct gradients, and the oracle's rate on the same shape."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from gated_linear_recurrence_history_amd import binding
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(5150)
+    grads = [(rng.standard_normal((rows, cols)) * 3.0).astype(np.float32) for _ in range(4)]
+    dg = [torch.from_numpy(g).to(dev) for g in grads]
+    out = torch.empty(cols, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, binding.lib().gscan_bias_grad_reduce_workspace_bytes(rows, cols)),
+                     dtype=torch.uint8, device=dev)
+    fns = [binding.prepare_bias_grad_reduce(g, out, ws, stream) for g in dg]
+    for i in range(20):
+        fns[i % len(fns)]()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(reps):
+        fns[i % len(fns)]()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    nbytes = rows * cols * 4 + cols * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.column_sums(grads[passes % len(grads)])
+        passes += 1
+        if time.perf_counter() - t0 > 0.5:
+            break
+    t = time.perf_counter() - t0
+    return {"entry": "gscan_bias_grad_reduce", "shape": [rows, cols], "us_per_call": round(us, 3),
+            "algorithmic_bytes": nbytes, "GBs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "oracle": {"us_per_call": round(t / passes * 1e6, 1), "cores": oracle.max_threads(),
+                       "sample": f"the same shape, {passes} calls in {t:.2f} s"}}
 
 
 def traffic_record(kernel, workload):
@@ -294,6 +345,8 @@ def main():
     }
     if not args.no_input_grads:
         out["input_grads"] = input_grads(args, w, sets, stream, k_bwd + k_red, reps)
+    if not args.no_bias_grad:
+        out["bias_grad_reduce"] = bias_grad(args, stream, reps)
     if args.copy_calibration_mib > 0:
         nb = args.copy_calibration_mib << 20
         src = torch.ones(nb, dtype=torch.uint8, device=dev)

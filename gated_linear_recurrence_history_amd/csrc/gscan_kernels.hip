@@ -1164,7 +1164,6 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     __shared__ float cvp[kWaves2][16][16];  // C partials of the current group
     __shared__ float dctl[16][16];          // d_context slice of the current group
     __shared__ float dCl[16][16];           // dL/dC = d_context * x_K
-    __shared__ float laml[16][16];          // lambda_K = d_context * C
     __shared__ f4 xch[kWaves2][2][kWave];   // partial projections (A, B)
     // per-wavefront transposition tile [plane hi|lo][row][column of the half],
     // rows padded by 8 columns so the 16 rows of a transposed read spread
@@ -1284,19 +1283,6 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         // the first unit's weight operands (the rest follow one unit ahead)
         Split wAn = wop(Wl, half * NH, 0, lane), wBn = wop(Wl, half * NH, 1, lane);
         __syncthreads();  // last step's exchange read; this group's C partials visible
-        if (c == 0) {
-            // lambda_K = dL/dx_K = d_context * C of the group's samples
-            if (wave < 4) {
-                int z;
-                asm volatile("s_mov_b32 %0, 0" : "=s"(z));  // keep the addresses local
-                const int bl = (tid + z) >> 4, s = (tid + z) & 15;
-                float cs = 0.f;
-#pragma unroll
-                for (int w = 0; w < kWaves2; ++w) cs += cvp[w][bl][s];
-                laml[bl][s] = dctl[bl][s] * cs;
-            }
-            __syncthreads();
-        }
         const int cb = c * kChunkRows;
         const int ce = cb + kChunkRows < NR ? cb + kChunkRows : NR;
         const int lr0 = cb + kBlockRows * blk;
@@ -1350,18 +1336,32 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             beta[j] = v ? aB[j] : 0.f;
         }
         // LDS values of the walks, read up front (clamped rows; used only
-        // where the row is valid): d_context at each row's sample, lambda_K
-        // of the sample of the lane's last row and of the sample before each
-        // row (a sample starting inside the lane when K < 4)
-        float dcv[4], lprev[4];
+        // where the row is valid): d_context at each row's sample, and
+        // lambda_K = dL/dx_K = d_context * C (C from the eight wavefronts'
+        // partials) of the sample of the lane's last row and, when K < 4, of
+        // the sample before each row (a sample starting inside the lane)
+        auto lam_k = [&](int sj, float dcs) {
+            float cs = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves2; ++w) cs += cvp[w][sj][ln];
+            return dcs * cs;
+        };
+        float dcv[4], lprev[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int sj = (lr0 + 4 * kg + j) >> kshift;
             dcv[j] = dctl[sj < 15 ? sj : 15][ln];
-            lprev[j] = laml[sj - 1 < 0 ? 0 : (sj - 1 < 15 ? sj - 1 : 15)][ln];
         }
         const int s3 = (lr0 + 4 * kg + 3) >> kshift;
-        const float llast = laml[s3 < 15 ? s3 : 15][ln];
+        const float llast = lam_k(s3 < 15 ? s3 : 15, dcv[3]);
+        if (K < 4) {
+#pragma unroll
+            for (int j = 1; j < 4; ++j) {
+                const int sj = (lr0 + 4 * kg + j) >> kshift;
+                const int sp = sj - 1 < 0 ? 0 : (sj - 1 < 15 ? sj - 1 : 15);
+                lprev[j] = lam_k(sp, dctl[sp][ln]);
+            }
+        }
 
         const int kgs = K >> 2;  // lane groups per sample (K >= 8: 2 or 4)
         const bool odd = kg & 1;

@@ -137,3 +137,53 @@ def test_graph_replays():
         assert np.array_equal(got_ctx, ref_ctx), i
         for a, b in zip(got, ref):
             assert np.array_equal(a, b), i
+
+
+def test_graph_replays_input_grads_and_bias_grad():
+    """gscan_backward_full_ex and gscan_bias_grad_reduce captured in one HIP
+    graph (caller workspaces, the general backward kernel's shape so the
+    adjoint kernel is in it too) and replayed with new inputs in between:
+    every replay equals eager calls on its inputs."""
+    w = workload(300, 5, 192, 32, seed=23)  # K = 5: the general kernel + adjoint pass
+    print("case graph replays (input grads, bias grad)", flush=True)
+    t = device_inputs(synth.make_inputs(w))
+    h = t["h_history"].clone()
+    d = t["d_context"].clone()
+    g = torch.empty((4099, 24), device=DEV)
+    nf = binding.backward_full_workspace_bytes(w.B, w.K, w.SH2, w.D)
+    wsf = torch.empty(nf, dtype=torch.uint8, device=DEV)
+    nb = binding.lib().gscan_bias_grad_reduce_workspace_bytes(4099, 24)
+    wsb = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    out = (tuple(torch.empty((w.SH2, w.D), device=DEV) for _ in range(3))
+           + (torch.empty((w.B * w.K, w.SH2), device=DEV), torch.empty((w.B, w.SH2), device=DEV)))
+    gsum = torch.empty(24, device=DEV)
+
+    def step():
+        gs.backward_full(h, t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K, d, 0.25, out=out,
+                         workspace=wsf)
+        gs.bias_grad_reduce(g, out=gsum, workspace=wsb)
+
+    g.normal_()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        h.copy_(t["h_history"] * (1.0 + 0.5 * i))
+        d.copy_(t["d_context"] * (0.5 - 0.25 * i))
+        g.copy_(torch.randn((4099, 24), device=DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.cpu().numpy() for o in out] + [gsum.cpu().numpy()]
+        ref = gs.backward_full(h, t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K, d, 0.25)
+        refg = gs.bias_grad_reduce(g)
+        torch.cuda.synchronize()
+        for a, b in zip(got, [r.cpu().numpy() for r in ref] + [refg.cpu().numpy()]):
+            assert np.array_equal(a, b), i

@@ -19,6 +19,10 @@ Fields beyond the headline value:
                     (profiles/traffic_<kernel>_<workload>.txt), else null
   cpu_baseline      the fp64 CPU oracle timed on a bounded sample of the
                     same workload on this host's cores
+  configs           every named workload (tiny, headline, long K, bf16 big
+                    batch, wide): forward and backward HIP-event time per call
+                    on resident synthetic inputs, samples/s and the fraction
+                    of 8 TB/s their algorithmic bytes reach
   bias_grad_reduce  the batch-parallel bias-gradient reduction on the spec's
                     IQN shape [524288 x 3] (fp32, synthetic N(0, 9)): HIP-event
                     time per call, bytes read against 8 TB/s, and the
@@ -65,6 +69,8 @@ def parse():
                     help="skip the timing of the backward with input gradients")
     ap.add_argument("--no-bias-grad", action="store_true",
                     help="skip the timing of the bias-gradient reduction")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload forward/backward timings")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finish with 4 untimed device copies of this many MiB (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -157,6 +163,55 @@ def input_grads(args, w, sets, stream, bwd_us, reps):
                        "cores": oracle.max_threads(),
                        "sample": f"first {ns} samples, fp64 input gradients, {passes} passes "
                                  f"in {t:.1f} s"}}
+
+
+def all_configs(stream):
+    """Forward and backward per call on every named workload (one input set
+    each; the larger ones exceed the 256 MB Infinity Cache by themselves)."""
+    import numpy as np
+    import torch
+
+    from gated_linear_recurrence_history_amd import binding, synth, workloads as wl
+
+    dev = torch.device("cuda:0")
+    res = {}
+    for w in wl.WORKLOADS:
+        x = synth.make_inputs(w)
+        t = {k: (torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
+                 if v.dtype == np.uint16 else torch.from_numpy(v).to(dev)) for k, v in x.items()}
+        del x
+        ctx = torch.empty((w.B, w.D), device=dev)
+        dW = tuple(torch.empty((w.SH2, w.D), device=dev) for _ in range(3))
+        ws = torch.empty(binding.backward_workspace_bytes(w.B, w.K, w.SH2, w.D,
+                                                          w.in_dtype == "bf16"),
+                         dtype=torch.uint8, device=dev)
+        a = (t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K)
+        f = binding.prepare_forward(*a, ctx, w.a_shift, stream)
+        b = binding.prepare_backward(*a, t["d_context"], dW, ws, w.a_shift, stream)
+        reps = max(5, min(200, int(2e8 // (w.fwd_bytes() + 1))))
+        times = {}
+        for name, fn in (("fwd", f), ("bwd", b)):
+            for _ in range(3):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[name] = e0.elapsed_time(e1) * 1e3 / reps
+        tot = times["fwd"] + times["bwd"]
+        byts = w.fwd_bytes() + w.bwd_bytes()
+        res[w.name] = {"B": w.B, "K": w.K, "SH2": w.SH2, "D": w.D, "in_dtype": w.in_dtype,
+                       "fwd_us": round(times["fwd"], 2), "bwd_us": round(times["bwd"], 2),
+                       "samples_per_s": round(w.B / (tot * 1e-6), 1),
+                       "hbm_frac": round(byts / (tot * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+                       "reps": reps}
+        del t, ctx, dW, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def bias_grad(args, stream, reps, rows=524288, cols=3):
@@ -347,6 +402,8 @@ def main():
         out["input_grads"] = input_grads(args, w, sets, stream, k_bwd + k_red, reps)
     if not args.no_bias_grad:
         out["bias_grad_reduce"] = bias_grad(args, stream, reps)
+    if not args.no_configs:
+        out["configs"] = all_configs(stream)
     if args.copy_calibration_mib > 0:
         nb = args.copy_calibration_mib << 20
         src = torch.ones(nb, dtype=torch.uint8, device=dev)

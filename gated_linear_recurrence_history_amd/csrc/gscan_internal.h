@@ -18,6 +18,7 @@ constexpr int kBlockRows = 16;     // h_history rows per wavefront block (MFMA M
 constexpr int kChunkRows = kBlockRows * kWaves;  // rows per backward chunk
 constexpr int kXcds = 8;           // MI355X accelerator complex dies
 constexpr int kMaxSH2 = 512;
+constexpr int64_t kFwdMaxRows = 512;
 constexpr int kMaxD = 256;
 
 struct Plan {
@@ -26,7 +27,8 @@ struct Plan {
     int nq = 0;             // SH2 / 32
     int slices = 0;         // D / 16
     int64_t groups = 0;     // ceil(B / 16)
-    int64_t fwd_rows = 0;   // group slots of the forward grid (multiple of 8)
+    int64_t fwd_rows = 0;   // group slots, one per group (multiple of 8)
+    int64_t fwd_prow = 0;   // persistent rows of the forward grid (<= kFwdMaxRows)
     int64_t bwd_rows = 0;   // persistent workgroup rows of the backward grid (multiple of 8)
     int64_t fwd_grid = 0;
     int64_t bwd_grid = 0;

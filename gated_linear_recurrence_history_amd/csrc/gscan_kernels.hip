@@ -611,6 +611,88 @@ gscan_fwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     }
 }
 
+template <typename TIn, int NQ>
+__global__ void __launch_bounds__(kThreads, NQ <= 8 ? 2 : 1)
+gscan_fwd_persist_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
+                 const float *__restrict__ WA, const float *__restrict__ WB,
+                 const float *__restrict__ WC, int64_t B, int K, int D, int slices,
+                 int64_t groups, int64_t nrows, float a_shift, float *__restrict__ ctx)
+{
+    constexpr int SH2 = NQ * 32;
+    __shared__ u4 Wl[NQ * 6 * kWave];
+    __shared__ float cvp[kWaves][16][16];
+    __shared__ f4 wraw[raw_rows_of(NQ) * 4];
+
+    // persistent over the groups g, g + nrows, ... of one state slice (more
+    // groups than grid rows): the weights are staged once per workgroup
+    int64_t g;
+    int slice;
+    decode_block(slices, g, slice);
+    if (g >= groups) return;
+    const int s0 = slice * kSlice;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int kg = lane >> 4, ln = lane & 15;
+    const int lr_begin = 4 * wave * K;
+    const LaneOff lo = lane_offsets(kg, K);
+    auto samples_of = [&](int64_t gg) {
+        return (int)(B - gg * kGroupSamples < kGroupSamples ? B - gg * kGroupSamples
+                                                            : kGroupSamples);
+    };
+    auto end_of = [&](int nb) { return (4 * wave + 4 < nb ? 4 * wave + 4 : nb) * K; };
+    // a row of group gg for this lane, clamped to the wavefront's last row
+    // (a valid row even for an idle wavefront: its end is at least K)
+    auto rowp = [&](int64_t gg, int lr_end, int base) {
+        const int r = base + ln;
+        return hh + gg * kGroupSamples * K * SH2 + (uint32_t)((r < lr_end ? r : lr_end - 1) * SH2);
+    };
+    auto cv_rows = [&](int64_t gg, int nb) {
+        return hs2 + gg * kGroupSamples * SH2 + (uint32_t)((ln < nb ? ln : nb - 1) * SH2);
+    };
+
+    // loads in the order they are consumed: weights, h_s2, first h block
+    int nb = samples_of(g);
+    int lr_end = end_of(nb);
+    WStage<NQ> wst;
+    wst.load(WA, WB, WC, D, s0);
+    CvLoad<TIn, NQ> cvl;
+    cvl.load(cv_rows(g, nb), wave, kg);
+    PBlk<TIn, NQ> b0buf, b1buf;
+    b0buf.load(rowp(g, lr_end, lr_begin), kg);
+    wst.store(Wl, reinterpret_cast<float *>(wraw));
+    for (;;) {
+        const int64_t b0 = g * kGroupSamples;
+        __syncthreads();  // weights staged; the previous group's readers of cvp done
+        {
+            const f4 cp = cvl.partial(Wl, wave, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cvp[wave][4 * kg + j][ln] = cp[j];
+        }
+        __syncthreads();
+        if (lr_begin < lr_end) {
+            // the next block is always requested (clamped to the last row past
+            // the end), so the wait for the current block leaves it in flight
+            float xc = 0.f;
+            for (int base = lr_begin; base < lr_end; base += 2 * kBlockRows) {
+                const int base1 = base + kBlockRows;
+                b1buf.load(rowp(g, lr_end, base1), kg);
+                fwd_block<TIn, NQ>(b0buf, Wl, base, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo,
+                                   xc, ctx);
+                if (base1 >= lr_end) break;
+                b0buf.load(rowp(g, lr_end, base1 + kBlockRows), kg);
+                fwd_block<TIn, NQ>(b1buf, Wl, base1, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo,
+                                   xc, ctx);
+            }
+        }
+        g += nrows;
+        if (g >= groups) break;
+        // the next group's C rows and first block go out before the barriers
+        nb = samples_of(g);
+        lr_end = end_of(nb);
+        cvl.load(cv_rows(g, nb), wave, kg);
+        b0buf.load(rowp(g, lr_end, lr_begin), kg);
+    }
+}
+
 // ============================================================= backward kernel
 constexpr int nsb_of(int nq) { return nq * 32 / 64; }
 constexpr int sbw_of(int nq) { return (nsb_of(nq) + kWaves - 1) / kWaves; }
@@ -1714,9 +1796,15 @@ hipError_t fwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
                       const float *WB, const float *WC, float a_shift, float *ctx,
                       hipStream_t st)
 {
-    hipLaunchKernelGGL((gscan_fwd_kernel<TIn, NQ>), dim3((unsigned)p.fwd_grid), dim3(kThreads), 0,
-                       st, static_cast<const TIn *>(hh), static_cast<const TIn *>(hs2), WA, WB,
-                       WC, p.B, (int)p.K, (int)p.D, p.slices, p.groups, a_shift, ctx);
+    if (p.fwd_prow < p.fwd_rows)
+        hipLaunchKernelGGL((gscan_fwd_persist_kernel<TIn, NQ>), dim3((unsigned)p.fwd_grid),
+                           dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
+                           static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
+                           p.slices, p.groups, p.fwd_prow, a_shift, ctx);
+    else
+        hipLaunchKernelGGL((gscan_fwd_kernel<TIn, NQ>), dim3((unsigned)p.fwd_grid), dim3(kThreads),
+                           0, st, static_cast<const TIn *>(hh), static_cast<const TIn *>(hs2), WA,
+                           WB, WC, p.B, (int)p.K, (int)p.D, p.slices, p.groups, a_shift, ctx);
     return hipGetLastError();
 }
 
@@ -1803,7 +1891,9 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
     q.slices = (int)(D / kSlice);
     q.groups = (B + kGroupSamples - 1) / kGroupSamples;
     q.fwd_rows = (q.groups + kXcds - 1) / kXcds * kXcds;
-    q.fwd_grid = q.fwd_rows * q.slices;
+    // forward: two workgroups per CU, persistent beyond 512 group slots
+    q.fwd_prow = q.fwd_rows < kFwdMaxRows ? q.fwd_rows : kFwdMaxRows;
+    q.fwd_grid = q.fwd_prow * q.slices;
     // backward: the rows kernel (K divides 16, SH2 <= 256) runs one persistent
     // workgroup per CU; the general kernel about two per CU when the weight
     // slice leaves room for two in LDS, one otherwise (256 CUs)

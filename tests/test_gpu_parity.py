@@ -48,6 +48,10 @@ SMALL = [
     (45, 2, 192, 16, "bf16", 0.5),
     (13, 16, 64, 48, "f32", 2.0),
     (70, 2, 256, 16, "f32", 0.0),
+    # more than 512 groups of 16 samples: the forward walks several groups
+    # per workgroup (ragged last group, two state slices)
+    (9000, 2, 64, 16, "f32", 0.5),
+    (8300, 4, 128, 32, "bf16", -1.0),
 ]
 
 

@@ -1823,16 +1823,20 @@ hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
             return hipGetLastError();
         }
     }
-    if (aligned)
-        hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ, true>), dim3((unsigned)p.bwd_grid),
-                           dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
-                           static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
-                           p.slices, p.groups, p.bwd_rows, a_shift, dctx, part, dab, dc);
-    else
-        hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ, false>), dim3((unsigned)p.bwd_grid),
-                           dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
-                           static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
-                           p.slices, p.groups, p.bwd_rows, a_shift, dctx, part, dab, dc);
+    // K dividing 16 with NQ <= 8 always takes the per-block kernel above
+    if constexpr (NQ > 8) {
+        if (aligned) {
+            hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ, true>), dim3((unsigned)p.bwd_grid),
+                               dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
+                               static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
+                               p.slices, p.groups, p.bwd_rows, a_shift, dctx, part, dab, dc);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gscan_bwd_kernel<TIn, NQ, false>), dim3((unsigned)p.bwd_grid),
+                       dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
+                       static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
+                       p.slices, p.groups, p.bwd_rows, a_shift, dctx, part, dab, dc);
     return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct Plan {
     int64_t fwd_prow = 0;   // persistent rows of the forward grid (<= kFwdMaxRows)
     int64_t bwd_rows = 0;   // persistent workgroup rows of the backward grid (multiple of 8)
     int64_t fwd_grid = 0;
+    int fwd_ms = 0;         // slices per workgroup of the multi-slice forward (0: one)
     int64_t bwd_grid = 0;
     int64_t red_grid = 0;
     bool bwd_rows_kernel = false;  // backward via the K-divides-16 kernel

@@ -693,6 +693,192 @@ gscan_fwd_persist_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2
     }
 }
 
+// =============================== forward, several state slices per workgroup
+// With D > 16 the kernels above re-read and re-split every row once per
+// 16-state slice.  Here a workgroup of 8 wavefronts takes two groups of 16
+// samples (wavefronts 0-3 and 4-7, four samples each) and S slices: each
+// 32-column unit of a row block is split once and multiplied with the A and
+// B weights of all S slices, held in LDS as one bf16 hi/lo image (S * SH2 *
+// 32 pairs, at most 128 KiB).  The C weights pass through the same LDS first,
+// for the C values of both groups.  The next block's unit q is requested as
+// soon as unit q of the current block has been split, so one register buffer
+// holds both blocks.
+constexpr int kWavesM = 8;
+constexpr int kThreadsM = kWave * kWavesM;
+
+// LDS image of NW weights over S slices: entry r = (s * NQ + q) * NW + w
+// holds, for lane l, rows 32q + 8(l/16) + 0..7 of weight w at state
+// s0 + 16s + l%16, split into bf16 high (u4 index 2r * 64 + l) and low
+// (index (2r + 1) * 64 + l).  Read straight from the fp32 weights: each
+// lane group of 16 reads 64 contiguous bytes of a row.
+template <int NQ, int S, int NW>
+__device__ __forceinline__ void stage_image(u4 *img, const float *__restrict__ W0,
+                                            const float *__restrict__ W1, int D, int s0)
+{
+    constexpr int kEnt = S * NQ * NW * kWave;
+    constexpr int kRounds = (kEnt + kThreadsM - 1) / kThreadsM;
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+        const int e = threadIdx.x + i * kThreadsM;
+        if (kEnt % kThreadsM == 0 || e < kEnt) {
+            const int lane = e & 63, r = e >> 6;
+            const int w = NW == 1 ? 0 : r % NW;
+            const int sq = r / NW, q = sq % NQ, s = sq / NQ;
+            const float *__restrict__ W = w == 0 ? W0 : W1;
+            const float *p = W + (32 * q + 8 * (lane >> 4)) * D + s0 + 16 * s + (lane & 15);
+            float x[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = p[k * D];
+            const Split sp = split8(x);
+            img[(2 * r) * kWave + lane] = sp.hi;
+            img[(2 * r + 1) * kWave + lane] = sp.lo;
+        }
+    }
+}
+
+__device__ __forceinline__ Split img_op(const u4 *img, int r, int lane)
+{
+    Split s;
+    s.hi = img[(2 * r) * kWave + lane];
+    s.lo = img[(2 * r + 1) * kWave + lane];
+    return s;
+}
+
+template <typename TIn, int NQ, int S>
+__global__ void __launch_bounds__(kThreadsM, 1)
+gscan_fwd_ms_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
+                    const float *__restrict__ WA, const float *__restrict__ WB,
+                    const float *__restrict__ WC, int64_t B, int K, int D, int sgroups,
+                    int64_t groups, float a_shift, float *__restrict__ ctx)
+{
+    constexpr int SH2 = NQ * 32;
+    constexpr bool LO = PBlk<TIn, NQ>::kLo;
+    constexpr int kImg = S * NQ * 4 * kWave;  // u4 entries of the A|B image
+    constexpr int kPart = 2 * 4 * S * 16 * 16 / 4;  // u4 entries of the C partials
+    __shared__ u4 img[kImg > kPart ? kImg : kPart];
+    __shared__ float cvs[2][S][16][16];  // C values of both groups
+
+    // (pair of groups, set of S slices); the slice sets of one pair run on one XCD
+    int64_t pr;
+    int sg;
+    decode_block(sgroups, pr, sg);
+    if (pr >= (groups + 1) / 2) return;  // whole workgroup
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int team = wave >> 2, wt = wave & 3;
+    const int kg = lane >> 4, ln = lane & 15;
+    const int s0 = sg * S * kSlice;
+    // the second group of a pair may lie past the batch: that team repeats
+    // the last group's loads and takes part in the barriers, writing nothing
+    const int64_t graw = 2 * pr + team;
+    const bool gvalid = graw < groups;
+    const int64_t g = gvalid ? graw : groups - 1;
+    const int64_t b0 = g * kGroupSamples;
+    const int nb = (int)(B - b0 < kGroupSamples ? B - b0 : kGroupSamples);
+    const int lr_begin = 4 * wt * K;
+    const int lr_end = (4 * wt + 4 < nb ? 4 * wt + 4 : nb) * K;
+    const TIn *__restrict__ hg = hh + b0 * K * SH2;
+    const LaneOff lo = lane_offsets(kg, K);
+    auto rowp = [&](int base) {
+        const int r = base + ln;
+        return hg + (uint32_t)((r < lr_end ? r : lr_end - 1) * SH2);
+    };
+
+    // C values: h_s2 units q = wt + 4i of the group against the C image
+    CvLoad<TIn, NQ> cvl;
+    cvl.load(hs2 + b0 * SH2 + (uint32_t)((ln < nb ? ln : nb - 1) * SH2), wt, kg);
+    PBlk<TIn, NQ> blk;
+    blk.load(rowp(lr_begin), kg);
+    stage_image<NQ, S, 1>(img, WC, WC, D, s0);
+    __syncthreads();
+    f4 cp[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        f4 acc = zero4();
+#pragma unroll
+        for (int i = 0; i < CvLoad<TIn, NQ>::kU; ++i) {
+            const int q = wt + kWaves * i;
+            const f4 t = mfma3<LO>(cvl.u[i].op(0), img_op(img, s * NQ + (q < NQ ? q : NQ - 1), lane), acc);
+            acc = q < NQ ? t : acc;
+        }
+        cp[s] = acc;
+    }
+    __syncthreads();  // C image read
+    float(*const pt)[4][S][16][16] = reinterpret_cast<float(*)[4][S][16][16]>(img);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pt[team][wt][s][4 * kg + j][ln] = cp[s][j];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 2 * S * 256; e += kThreadsM) {
+        const int tm = e / (S * 256), s = (e / 256) % S, bl = (e >> 4) & 15, l = e & 15;
+        cvs[tm][s][bl][l] = (pt[tm][0][s][bl][l] + pt[tm][1][s][bl][l]) +
+                            (pt[tm][2][s][bl][l] + pt[tm][3][s][bl][l]);
+    }
+    __syncthreads();  // partials read before the A|B image overwrites them
+    stage_image<NQ, S, 2>(img, WA, WB, D, s0);
+    __syncthreads();
+    if (!gvalid || lr_begin >= lr_end) return;
+
+    float xc[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) xc[s] = 0.f;
+    for (int base = lr_begin; base < lr_end; base += kBlockRows) {
+        // the next block's rows (clamped past the end) replace this block's
+        // unit by unit
+        const TIn *__restrict__ nrow = rowp(base + kBlockRows);
+        f4 aA[S], aB[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            aA[s] = zero4();
+            aB[s] = zero4();
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const Split h = blk.op(q);
+            blk.load_unit(nrow, kg, q);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                aA[s] = mfma3<LO>(h, img_op(img, (s * NQ + q) * 2, lane), aA[s]);
+                aB[s] = mfma3<LO>(h, img_op(img, (s * NQ + q) * 2 + 1, lane), aB[s]);
+            }
+            // keep later units' operand reads from being hoisted further
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const RowPos bp = base_pos(base, K);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            Aff map[4];
+            Aff F = aff_id();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = base + 4 * kg + j;
+                Aff m;
+                if (r >= lr_end) {
+                    m = aff_id();
+                } else {
+                    m.m = sigmoid(aA[s][j] + a_shift);
+                    m.c = aB[s][j];
+                    m.r = row_pos(bp, lo, j, K).t == 0;
+                }
+                map[j] = m;
+                F = compose(m, F);
+            }
+            Aff excl, total;
+            scan_up(F, lane, excl, total);
+            float x = apply(excl, xc[s]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x = apply(map[j], x);
+                const int r = base + 4 * kg + j;
+                const RowPos rp = row_pos(bp, lo, j, K);
+                if (r < lr_end && rp.t == K - 1)
+                    ctx[(b0 + rp.bl) * D + s0 + 16 * s + ln] = cvs[team][s][rp.bl][ln] * x;
+            }
+            xc[s] = apply(total, xc[s]);
+        }
+    }
+}
+
 // ============================================================= backward kernel
 constexpr int nsb_of(int nq) { return nq * 32 / 64; }
 constexpr int sbw_of(int nq) { return (nsb_of(nq) + kWaves - 1) / kWaves; }
@@ -1796,6 +1982,23 @@ hipError_t fwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
                       const float *WB, const float *WC, float a_shift, float *ctx,
                       hipStream_t st)
 {
+    if (p.fwd_ms == 4) {
+        if constexpr (4 * NQ <= 32) {
+            hipLaunchKernelGGL((gscan_fwd_ms_kernel<TIn, NQ, 4>), dim3((unsigned)p.fwd_grid),
+                               dim3(kThreadsM), 0, st, static_cast<const TIn *>(hh),
+                               static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K,
+                               (int)p.D, p.slices / 4, p.groups, a_shift, ctx);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    if (p.fwd_ms == 2) {
+        hipLaunchKernelGGL((gscan_fwd_ms_kernel<TIn, NQ, 2>), dim3((unsigned)p.fwd_grid),
+                           dim3(kThreadsM), 0, st, static_cast<const TIn *>(hh),
+                           static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
+                           p.slices / 2, p.groups, a_shift, ctx);
+        return hipGetLastError();
+    }
     if (p.fwd_prow < p.fwd_rows)
         hipLaunchKernelGGL((gscan_fwd_persist_kernel<TIn, NQ>), dim3((unsigned)p.fwd_grid),
                            dim3(kThreads), 0, st, static_cast<const TIn *>(hh),
@@ -1895,9 +2098,21 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
     q.slices = (int)(D / kSlice);
     q.groups = (B + kGroupSamples - 1) / kGroupSamples;
     q.fwd_rows = (q.groups + kXcds - 1) / kXcds * kXcds;
-    // forward: two workgroups per CU, persistent beyond 512 group slots
+    // forward: two workgroups per CU, persistent beyond 512 group slots;
+    // for D > 16, S = 4 or 2 slices per workgroup of two groups when the A|B
+    // image fits (S * SH2 <= 1024) and either the scans are long enough to
+    // amortise staging it (K >= 16) or there are few groups
     q.fwd_prow = q.fwd_rows < kFwdMaxRows ? q.fwd_rows : kFwdMaxRows;
     q.fwd_grid = q.fwd_prow * q.slices;
+    q.fwd_ms = 0;
+    if (q.slices >= 2 && (K >= 16 || q.groups <= kFwdMaxRows)) {
+        for (int sv = 4; sv >= 2; sv /= 2)
+            if (q.fwd_ms == 0 && q.slices % sv == 0 && sv * q.nq <= 32) q.fwd_ms = sv;
+    }
+    if (q.fwd_ms) {
+        const int64_t pairs = (q.groups + 1) / 2;
+        q.fwd_grid = (pairs + kXcds - 1) / kXcds * kXcds * (q.slices / q.fwd_ms);
+    }
     // backward: the rows kernel (K divides 16, SH2 <= 256) runs one persistent
     // workgroup per CU; the general kernel about two per CU when the weight
     // slice leaves room for two in LDS, one otherwise (256 CUs)

@@ -52,6 +52,12 @@ SMALL = [
     # per workgroup (ragged last group, two state slices)
     (9000, 2, 64, 16, "f32", 0.5),
     (8300, 4, 128, 32, "bf16", -1.0),
+    # D > 16: several state slices per forward workgroup of two groups
+    # (a missing second group, bf16 rows, samples straddling blocks, more
+    # groups than grid slots in one pass)
+    (40, 16, 256, 64, "bf16", 0.5),
+    (33, 20, 384, 32, "f32", -0.5),
+    (9000, 16, 64, 32, "f32", 1.0),
 ]
 
 

@@ -1346,11 +1346,13 @@ struct BTask {
     int n;      // ordinal of the chunk in this workgroup
 };
 
-// ============================================ backward, K dividing 16 ("rows")
+// ================================= backward, K dividing 16, or 32, 64 ("rows")
 // When K divides 16 every 16-row block holds whole samples, so the block's
 // scans need nothing from other blocks: projection replay, forward and
 // reverse scans, and the weight-gradient contraction over the block's own
-// 16 rows.  That contraction needs h with rows along the MFMA k index,
+// 16 rows.  With K = 32 or 64 a sample fills 2 or 4 blocks of one 64-row
+// chunk, and one exchange of the blocks' state maps through LDS completes
+// the scans.  The contraction needs h with rows along the MFMA k index,
 // while the row loads put columns along k.  The split block (bf16 high and
 // low planes) goes to a per-wavefront LDS tile right after the split, and
 // ds_read_b64_tr_b16 reads it back transposed: four rows of one column per
@@ -1433,6 +1435,7 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     __shared__ float dctl[16][16];          // d_context slice of the current group
     __shared__ float dCl[16][16];           // dL/dC = d_context * x_K
     __shared__ f4 xch[kWaves2][2][kWave];   // partial projections (A, B)
+    __shared__ float bmap[4][2][16];         // per-block state maps (K >= 32)
     // per-wavefront transposition tile [plane hi|lo][row][column of the half],
     // rows padded by 8 columns so the 16 rows of a transposed read spread
     // over the banks; doubles as the raw tile of the weight staging and, at
@@ -1455,7 +1458,7 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     const int lane = tid & 63, wave = wave_id();
     const int kg = lane >> 4, ln = lane & 15;
     const int blk = wave & 3, half = wave >> 2;
-    const int kshift = __builtin_ctz((unsigned)K);  // K is a power of two <= 16
+    const int kshift = __builtin_ctz((unsigned)K);  // K: a power of two <= 16, or 32, 64
     uint16_t *const tile = reinterpret_cast<uint16_t *>(stage_mem) + wave * kPlanes * 16 * kPitch;
     uint16_t *const hst = reinterpret_cast<uint16_t *>(hst_mem) + wave * kPlanes * 16 * 32;
     float(*const red)[2][SH2][16] = reinterpret_cast<float(*)[2][SH2][16]>(stage_mem);
@@ -1631,10 +1634,12 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             }
         }
 
-        const int kgs = K >> 2;  // lane groups per sample (K >= 8: 2 or 4)
+        const int kgs = K >> 2;  // lane groups per sample (K >= 8: 2, or 4 and more)
         const bool odd = kg & 1;
         const float G = gate[0] * gate[1] * gate[2] * gate[3];
         float x_in = 0.f, gsuf = 1.f;  // state entering the lane; gates of later groups
+        float mx = 1.f;                // gate product of the block's earlier groups
+        float tM = 1.f, tC = 0.f;      // the block's map (K >= 32)
         if (kgs > 1) {
             // forward: affine map (M, C) of the lane's rows, composed over the
             // sample's lane groups; first within pairs of groups, then (K = 16)
@@ -1653,20 +1658,49 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             gsuf = odd ? 1.f : pg.hi;
             if (kgs > 2) {
                 // the first pair's total (held by its odd group) into rows 2-3
-                const float tM = pair_rows(M).hi, tC = pair_rows(C).hi;
-                const float fM = half_rows(tM).lo, fC = half_rows(tC).lo;
+                const float pM = pair_rows(M).hi, pC = pair_rows(C).hi;
+                const float fM = half_rows(pM).lo, fC = half_rows(pC).lo;
                 const bool second = kg >= 2;
                 if (second) {
                     C = M * fC + C;
                     M = M * fM;
                 }
-                const float cl = pair_rows(C).lo;  // (all lanes take part)
-                x_in = odd ? cl : (second ? fC : 0.f);
+                const RowVals qm = pair_rows(M), qc = pair_rows(C);  // (all lanes take part)
+                x_in = odd ? qc.lo : (second ? fC : 0.f);
+                mx = odd ? qm.lo : (second ? fM : 1.f);
                 const float hP = half_rows(pg.lo * pg.hi).hi;  // the second pair's gates
                 if (!second) gsuf *= hP;
+                if (K >= 32) {
+                    // the last group's inclusive map is the block's
+                    tM = half_rows(qm.hi).hi;
+                    tC = half_rows(qc.hi).hi;
+                }
             } else {
                 x_in = odd ? pc.lo : 0.f;
             }
+        }
+
+        if (K >= 32) {
+            // a sample spans 2 or 4 blocks of the chunk: the blocks' maps
+            // through LDS give the state entering this block and the gate
+            // product of the sample's later blocks (samples start at chunk
+            // starts, so none reaches into another chunk)
+            if (half == 0 && kg == 0) {
+                bmap[blk][0][ln] = tM;
+                bmap[blk][1][ln] = tC;
+            }
+            __syncthreads();
+            const int sb = lr0 >> kshift;
+            float X = 0.f, Ga = 1.f;
+#pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2) {
+                const bool same = ((cb + kBlockRows * b2) >> kshift) == sb;
+                const float bm = bmap[b2][0][ln], bc = bmap[b2][1][ln];
+                if (same && b2 < blk) X = bm * X + bc;
+                if (same && b2 > blk) Ga *= bm;
+            }
+            x_in = mx * X + x_in;
+            gsuf *= Ga;
         }
 
         // forward walk: state before each row, dL/dC at sample ends
@@ -2113,10 +2147,10 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
         const int64_t pairs = (q.groups + 1) / 2;
         q.fwd_grid = (pairs + kXcds - 1) / kXcds * kXcds * (q.slices / q.fwd_ms);
     }
-    // backward: the rows kernel (K divides 16, SH2 <= 256) runs one persistent
+    // backward: the rows kernel (K divides 16 or is 32 or 64, SH2 <= 256) runs one persistent
     // workgroup per CU; the general kernel about two per CU when the weight
     // slice leaves room for two in LDS, one otherwise (256 CUs)
-    q.bwd_rows_kernel = 16 % K == 0 && q.nq <= 8;
+    q.bwd_rows_kernel = (16 % K == 0 || K == 32 || K == 64) && q.nq <= 8;
     const int64_t target = (q.bwd_rows_kernel || q.nq > 8) ? 256 : 512;
     int64_t cap = target / q.slices / kXcds * kXcds;
     if (cap < kXcds) cap = kXcds;

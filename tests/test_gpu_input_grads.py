@@ -34,6 +34,8 @@ SHAPES = [
     (37, 16, 256, 48, "f32", 1.0),    # three state slices
     (45, 2, 192, 16, "bf16", 0.5),
     (70, 2, 256, 16, "f32", 0.0),
+    (21, 32, 128, 32, "f32", -1.0),   # samples of 2 blocks (per-block kernel)
+    (9, 64, 64, 16, "bf16", 0.5),     # samples of 4 blocks
 ]
 
 

@@ -58,6 +58,13 @@ SMALL = [
     (40, 16, 256, 64, "bf16", 0.5),
     (33, 20, 384, 32, "f32", -0.5),
     (9000, 16, 64, 32, "f32", 1.0),
+    # K = 32 or 64 with SH2 <= 256 (the per-block backward kernel): a sample
+    # fills 2 or 4 blocks of a chunk
+    (21, 32, 128, 16, "f32", 0.0),
+    (9, 64, 64, 32, "bf16", -0.5),
+    (13, 32, 256, 48, "f32", 2.0),
+    (6, 64, 192, 16, "f32", 1.0),
+    (35, 32, 256, 16, "f32", -3.0),
 ]
 
 

@@ -1417,15 +1417,18 @@ __device__ __forceinline__ f4 contract_op(const u4 &a, const GradOp &g, f4 acc)
 constexpr int kWaves2 = 8;
 constexpr int kThreads2 = kWave * kWaves2;
 
-template <typename TIn, int NQ>
+// KT: the scan length when fixed at compile time (the index arithmetic and
+// the branches on K then fold), 0 to take it from the argument.
+template <typename TIn, int NQ, int KT>
 __global__ void __launch_bounds__(kThreads2, 1)
 gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                       const float *__restrict__ WA, const float *__restrict__ WB,
-                      const float *__restrict__ WC, int64_t B, int K, int D, int slices,
+                      const float *__restrict__ WC, int64_t B, int Kin, int D, int slices,
                       int64_t groups, int64_t nrows, float a_shift,
                       const float *__restrict__ dctx, float *__restrict__ part,
                       float *__restrict__ dab_out, float *__restrict__ dc_out)
 {
+    const int K = KT ? KT : Kin;
     constexpr int SH2 = NQ * 32;
     constexpr int NH = NQ / 2;        // units per column half
     constexpr int HC = SH2 / 2;       // columns per half
@@ -2053,11 +2056,17 @@ hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
     const bool aligned = 16 % p.K == 0;
     if constexpr (NQ <= 8) {
         if (p.bwd_rows_kernel) {
-            hipLaunchKernelGGL((gscan_bwd_rows_kernel<TIn, NQ>), dim3((unsigned)p.bwd_grid),
-                               dim3(kThreads2), 0, st, static_cast<const TIn *>(hh),
-                               static_cast<const TIn *>(hs2), WA, WB, WC, p.B, (int)p.K, (int)p.D,
-                               p.slices, p.groups, p.bwd_rows, a_shift, dctx, part, dab, dc);
-            return hipGetLastError();
+            auto go = [&](auto kern) {
+                hipLaunchKernelGGL(kern, dim3((unsigned)p.bwd_grid), dim3(kThreads2), 0, st,
+                                   static_cast<const TIn *>(hh), static_cast<const TIn *>(hs2), WA,
+                                   WB, WC, p.B, (int)p.K, (int)p.D, p.slices, p.groups,
+                                   p.bwd_rows, a_shift, dctx, part, dab, dc);
+                return hipGetLastError();
+            };
+            // K = 8 (the spec's history length) and K = 64 run with K folded in
+            if (p.K == 8) return go(gscan_bwd_rows_kernel<TIn, NQ, 8>);
+            if (p.K == 64) return go(gscan_bwd_rows_kernel<TIn, NQ, 64>);
+            return go(gscan_bwd_rows_kernel<TIn, NQ, 0>);
         }
     }
     // K dividing 16 with NQ <= 8 always takes the per-block kernel above

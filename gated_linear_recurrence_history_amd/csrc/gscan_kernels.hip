@@ -1464,7 +1464,6 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     const int kshift = __builtin_ctz((unsigned)K);  // K: a power of two <= 16, or 32, 64
     uint16_t *const tile = reinterpret_cast<uint16_t *>(stage_mem) + wave * kPlanes * 16 * kPitch;
     uint16_t *const hst = reinterpret_cast<uint16_t *>(hst_mem) + wave * kPlanes * 16 * 32;
-    float(*const red)[2][SH2][16] = reinterpret_cast<float(*)[2][SH2][16]>(stage_mem);
 
     f4 accA[NQ], accB[NQ], accC[2];  // i-tiles of this half; dW_C unit `wave`
 #pragma unroll
@@ -1813,43 +1812,45 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     }
 
     // sums over the four blocks of each half: (b0 + b2) + (b1 + b3), in LDS
-    // (over the transposition tiles, once every wavefront is done with its own)
+    // (over the transposition tiles, once every wavefront is done with its
+    // own).  Layout [r][A|B][i/4][s][i%4]: a lane's four consecutive rows i
+    // of one state are one 16-byte entry and a wavefront's entries one
+    // contiguous KiB, so the writes and reads are 128-bit and free of bank
+    // conflicts.  The workgroup partial keeps that layout ("quad" layout:
+    // [which][i/4][s][i%4] over the full D); phase 2 maps it back to [i][s].
     __syncthreads();
+    f4 (*const redq)[2][SH2 / 4][16] = reinterpret_cast<f4 (*)[2][SH2 / 4][16]>(stage_mem);
     auto put = [&](int r, bool add) {
 #pragma unroll
-        for (int tl = 0; tl < NQ; ++tl)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = HC * half + 16 * tl + 4 * kg + j;
-                float &ra = red[r][0][i][ln];
-                float &rb = red[r][1][i][ln];
-                ra = add ? ra + accA[tl][j] : accA[tl][j];
-                rb = add ? rb + accB[tl][j] : accB[tl][j];
-            }
+        for (int tl = 0; tl < NQ; ++tl) {
+            const int iq = (HC * half + 16 * tl) / 4 + kg;
+            f4 &ra = redq[r][0][iq][ln];
+            f4 &rb = redq[r][1][iq][ln];
+            ra = add ? ra + accA[tl] : accA[tl];
+            rb = add ? rb + accB[tl] : accB[tl];
+        }
     };
     if (blk < 2) put(blk, false);
     __syncthreads();
     if (blk >= 2) put(blk - 2, true);
     __syncthreads();
-    // this workgroup's partial: part[rho][which][i][s]
+    // this workgroup's partial: part[rho][which][i/4][s][i%4]
     float *P = part + rho * 3 * (int64_t)SH2 * D;
-    constexpr int kVec = 2 * SH2 * 16 / 4;  // f4 entries of [A|B][i][s]
+    constexpr int kVec = 2 * SH2 * 16 / 4;  // f4 entries of [A|B][i/4][s]
     for (int v = tid; v < kVec; v += kThreads2) {
         const int which = v / (SH2 * 4);
         const int rem = v - which * SH2 * 4;
-        const int i = rem >> 2, s4 = (rem & 3) * 4;
-        const f4 r0 = *reinterpret_cast<const f4 *>(&red[0][which][i][s4]);
-        const f4 r1 = *reinterpret_cast<const f4 *>(&red[1][which][i][s4]);
-        *reinterpret_cast<f4 *>(P + which * (int64_t)SH2 * D + (int64_t)i * D + s0 + s4) = r0 + r1;
+        const int iq = rem >> 4, s = rem & 15;
+        const f4 r0 = redq[0][which][iq][s];
+        const f4 r1 = redq[1][which][iq][s];
+        *reinterpret_cast<f4 *>(P + which * (int64_t)SH2 * D + ((int64_t)iq * D + s0 + s) * 4) = r0 + r1;
     }
     if (wave < NQ) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = 32 * wave + 16 * t + 4 * kg + j;
-                P[2 * (int64_t)SH2 * D + (int64_t)col * D + s0 + ln] = accC[t][j];
-            }
+        for (int t = 0; t < 2; ++t) {
+            const int iq = (32 * wave + 16 * t) / 4 + kg;
+            *reinterpret_cast<f4 *>(P + 2 * (int64_t)SH2 * D + ((int64_t)iq * D + s0 + ln) * 4) = accC[t];
+        }
     }
 }
 
@@ -1862,7 +1863,7 @@ constexpr int kRedCols = 32;
 constexpr int kRedSegs = kThreads / (kRedCols / 4);
 
 __global__ void __launch_bounds__(kThreads)
-gscan_reduce_kernel(const float *__restrict__ part, int64_t nrows, int64_t wsz,
+gscan_reduce_kernel(const float *__restrict__ part, int64_t nrows, int64_t wsz, int D, int qlay,
                     float *__restrict__ dWA, float *__restrict__ dWB, float *__restrict__ dWC)
 {
     __shared__ double red[kRedSegs][kRedCols];
@@ -1897,7 +1898,10 @@ gscan_reduce_kernel(const float *__restrict__ part, int64_t nrows, int64_t wsz,
         const int64_t oo = (int64_t)blockIdx.x * kRedCols + t;
         const int64_t which = oo / wsz, e = oo - which * wsz;
         float *out = which == 0 ? dWA : (which == 1 ? dWB : dWC);
-        out[e] = (float)v;
+        // quad layout [i/4][s][i%4] -> [i][s]
+        const int64_t q = e >> 2;
+        const int64_t eo = qlay ? ((q / D) * 4 + (e & 3)) * D + q % D : e;
+        out[eo] = (float)v;
     }
 }
 
@@ -2237,8 +2241,10 @@ hipError_t launch_dinput(const float *in, const float *W1, const float *W2, int6
 hipError_t launch_backward_reduce(const Plan &p, const float *part, float *dWA, float *dWB,
                                   float *dWC, hipStream_t st)
 {
+    // the per-block kernel writes its partials in the quad layout
     hipLaunchKernelGGL(gscan_reduce_kernel, dim3((unsigned)p.red_grid), dim3(kThreads), 0, st,
-                       part, p.bwd_rows, p.SH2 * p.D, dWA, dWB, dWC);
+                       part, p.bwd_rows, p.SH2 * p.D, (int)p.D, p.bwd_rows_kernel ? 1 : 0, dWA,
+                       dWB, dWC);
     return hipGetLastError();
 }
 

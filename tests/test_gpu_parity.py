@@ -65,6 +65,12 @@ SMALL = [
     (13, 32, 256, 48, "f32", 2.0),
     (6, 64, 192, 16, "f32", 1.0),
     (35, 32, 256, 16, "f32", -3.0),
+    # K = 8 and 64 run the per-block backward compiled for that K: every
+    # SH2 it takes, ragged batches, several state slices, both input types
+    (27, 8, 128, 32, "f32", -1.0),
+    (45, 8, 64, 16, "f32", 0.5),
+    (29, 8, 192, 48, "bf16", 2.0),
+    (19, 64, 128, 16, "f32", 0.0),
 ]
 
 

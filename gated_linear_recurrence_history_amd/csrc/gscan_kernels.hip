@@ -1800,8 +1800,16 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         wst.load(WA, WB, WC, D, s0);
         const BTask t0 = {cur.g < groups ? cur.g : groups - 1, 0, 0, 0};
         load_group(t0.g);
-        load_chunk(t0, pA);
+        // the first chunk's rows go out in two halves, before and after the
+        // weight staging (measured faster than all of them before or after)
+        constexpr int kPre = NH / 2 > 0 ? NH / 2 : NH;
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) pA.load_unit(chunk_row(t0), kg, u);
+        __builtin_amdgcn_sched_barrier(0);
         wst.store(Wl, reinterpret_cast<float *>(stage_mem));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = kPre; u < NH; ++u) pA.load_unit(chunk_row(t0), kg, u);
     }
     __syncthreads();  // weights staged
     if (cur.g < groups) use_group(samples_of(cur.g));

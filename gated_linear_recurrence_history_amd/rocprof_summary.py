@@ -5,7 +5,13 @@ kept under profiles/.
     python -m gated_linear_recurrence_history_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR OUT \
         --kernel gscan_bwd_kernel --workload prod_fp32 --copy-bytes N --command "..."
 
+    python -m gated_linear_recurrence_history_amd.rocprof_summary counters OUT DIR [DIR ...] \
+        --kernel NAME [--kernel NAME ...] --command "..."
+
 ``stats`` keeps rocprofv3's own per-kernel statistics (kernel_stats.csv).
+``counters`` gives, for each named kernel, the mean per dispatch of every
+counter or derived metric the given ``--pmc`` runs collected (rows of one
+dispatch summed, as rocprofv3 writes one row per instance).
 ``traffic`` turns two counter runs (FETCH_SIZE, then WRITE_SIZE; both in KiB
 per dispatch) into HBM bytes per launch of one kernel.  Each counter is
 scaled by what it reads for a plain device-to-device copy of ``copy-bytes``
@@ -132,6 +138,43 @@ def write_traffic(fetch_dir, write_dir, out_path, kernel, workload, copy_bytes, 
     return rec
 
 
+def counter_names(directory: str):
+    """Counter and metric names present in one counter_collection.csv, in file order."""
+    path = _find(directory, "counter_collection.csv")
+    with open(path, newline="") as f:
+        rows = list(csv.reader(f))
+    icn = _col(rows[0], "counter_name")
+    seen = []
+    for r in rows[1:]:
+        if r[icn] not in seen:
+            seen.append(r[icn])
+    return seen
+
+
+def write_counters(dirs, out_path, kernels, command):
+    """Mean per dispatch of every collected counter for each kernel; returns {kernel: {counter: v}}."""
+    table = {k: {} for k in kernels}
+    counts = {k: {} for k in kernels}
+    for d in dirs:
+        for c in counter_names(d):
+            per = counter_per_dispatch(d, c)
+            for k in kernels:
+                if k in per:
+                    table[k][c] = statistics.mean(per[k])
+                    counts[k][c] = len(per[k])
+    lines = ["rocprofv3 counters per dispatch (mean over dispatches)", "",
+             f"commands: {command}", ""]
+    for k in kernels:
+        lines.append(k)
+        for c, v in table[k].items():
+            lines.append(f"  {c:<34} {v:>18.4f}   ({counts[k][c]} dispatches)")
+        lines.append("")
+    lines.append("record: " + json.dumps(table))
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return table
+
+
 def read_traffic(path):
     """The record of a traffic summary, or None if absent or unparsable."""
     try:
@@ -160,9 +203,16 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--copies", type=int, default=4)
     t.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("out")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.mode == "stats":
         write_stats(a.dir, a.out, a.command)
+    elif a.mode == "counters":
+        print(json.dumps(write_counters(a.dirs, a.out, a.kernel, a.command)))
     else:
         print(json.dumps(write_traffic(a.fetch_dir, a.write_dir, a.out, a.kernel, a.workload,
                                        a.copy_bytes, a.copies, a.command)))

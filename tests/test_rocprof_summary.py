@@ -46,3 +46,16 @@ def test_stats(tmp_path):
     rs.write_stats(str(d), str(tmp_path / "o.txt"), "cmd")
     text = (tmp_path / "o.txt").read_text()
     assert "gscan_fwd_kernel<float, 8>" in text and "20.000" in text and "command: cmd" in text
+
+
+def test_counters_mean_per_dispatch(tmp_path):
+    k = "void gscan::(anonymous namespace)::gscan_fwd_kernel<float, 8>(float const*)"
+    other = "void gscan::(anonymous namespace)::gscan_reduce_kernel(float const*)"
+    _counters(tmp_path / "a", "SQ_INSTS_MFMA", [(1, k, 10.0), (1, k, 30.0), (2, other, 7.0),
+                                               (3, k, 60.0)])
+    _counters(tmp_path / "b", "MfmaUtil", [(4, k, 12.5), (5, k, 13.5), (6, other, 1.0)])
+    t = rs.write_counters([str(tmp_path / "a"), str(tmp_path / "b")], str(tmp_path / "c.txt"),
+                          ["gscan_fwd_kernel<float, 8>"], "cmd")
+    assert t == {"gscan_fwd_kernel<float, 8>": {"SQ_INSTS_MFMA": 50.0, "MfmaUtil": 13.0}}
+    text = (tmp_path / "c.txt").read_text()
+    assert "SQ_INSTS_MFMA" in text and "commands: cmd" in text

@@ -1842,7 +1842,9 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     __syncthreads();
     if (blk >= 2) put(blk - 2, true);
     __syncthreads();
-    // this workgroup's partial: part[rho][which][i/4][s][i%4]
+    // this workgroup's partial: part[rho][which][i/4][s][i%4], written with
+    // non-temporal stores (read once, by phase 2, from beyond the L2s: the
+    // end of the kernel then has no partials to write back from L2)
     float *P = part + rho * 3 * (int64_t)SH2 * D;
     constexpr int kVec = 2 * SH2 * 16 / 4;  // f4 entries of [A|B][i/4][s]
     for (int v = tid; v < kVec; v += kThreads2) {
@@ -1851,13 +1853,15 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         const int iq = rem >> 4, s = rem & 15;
         const f4 r0 = redq[0][which][iq][s];
         const f4 r1 = redq[1][which][iq][s];
-        *reinterpret_cast<f4 *>(P + which * (int64_t)SH2 * D + ((int64_t)iq * D + s0 + s) * 4) = r0 + r1;
+        __builtin_nontemporal_store(
+            r0 + r1, reinterpret_cast<f4 *>(P + which * (int64_t)SH2 * D + ((int64_t)iq * D + s0 + s) * 4));
     }
     if (wave < NQ) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int iq = (32 * wave + 16 * t) / 4 + kg;
-            *reinterpret_cast<f4 *>(P + 2 * (int64_t)SH2 * D + ((int64_t)iq * D + s0 + ln) * 4) = accC[t];
+            __builtin_nontemporal_store(
+                accC[t], reinterpret_cast<f4 *>(P + 2 * (int64_t)SH2 * D + ((int64_t)iq * D + s0 + ln) * 4));
         }
     }
 }

@@ -9,6 +9,11 @@ is real HBM traffic.  Prints one JSON line.
 
 Fields beyond the headline value:
   hbm_frac          algorithmic bytes per step / step time / 8 TB/s
+  step_us           p10 / p50 / p90 of single-step times (an event pair
+                    around each step, measured after the timed region)
+  copy_GBs          a measured streaming ceiling for context: bytes read
+                    plus written by a 512 MiB device-to-device copy over its
+                    time (median of 5)
   kernels_us        average duration of each kernel: HIP events on the
                     launch stream around a run of back-to-back launches of
                     that kernel alone
@@ -355,6 +360,37 @@ def main():
     k_bwd = per_launch_us(lambda i: bwd1[i % n]())
     k_red = per_launch_us(lambda i: red())
 
+    # ---- spread of single steps (outside the timed region): an event pair
+    # around each of `reps` steps, then percentiles of the per-step times
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        fwd[i % n]()
+        bwd[i % n]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    step_us = {q: round(float(np.percentile(per_step, pq)), 3)
+               for q, pq in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+    # ---- a measured streaming ceiling for context: a device-to-device copy
+    # of 512 MiB (read + write bytes over its HIP-event time, median of 5)
+    cb = 512 << 20
+    csrc = torch.empty(cb, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    ctimes = []
+    for _ in range(6):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cdst.copy_(csrc)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ctimes.append(a.elapsed_time(b) * 1e-3)
+    copy_gbs = 2 * cb / float(np.median(ctimes[1:])) / 1e9
+    del csrc, cdst
+
     step_bytes = w.fwd_bytes() + w.bwd_bytes()
     value = w.B / (ms_step * 1e-3)
     hbm_frac = step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
@@ -393,6 +429,8 @@ def main():
         "config": dict(w.describe(), input_sets=args.sets),
         "hbm_frac": round(hbm_frac, 4),
         "hbm_GBs_fwd_bwd": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_us": step_us,
+        "copy_GBs": round(copy_gbs, 1),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
         "kernels_us": {"gscan_fwd_kernel": round(k_fwd, 3), "backward_phase1": round(k_bwd, 3),
                        "gscan_reduce_kernel": round(k_red, 3)},

@@ -93,3 +93,15 @@ def test_traffic_model_matches_page_arithmetic():
     assert w.fwd_bytes() == 76_070_912
     assert w.bwd_bytes() == 76_120_064
     assert (w.fwd_bytes() + w.bwd_bytes()) // w.B == 18_578
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it exits at once with a message
+    (before touching torch or a device)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr

@@ -403,8 +403,10 @@ def main():
     # dominant kernel against HBM (its MFMA time, 3 bf16 products per fp32
     # product at the bf16 peak, is far below its HBM time)
     if k_bwd >= k_fwd:
-        # K dividing 16 with SH2 <= 256 runs the per-block backward kernel
-        bname = "gscan_bwd_rows_kernel" if 16 % w.K == 0 and w.SH2 <= 256 else "gscan_bwd_kernel"
+        # K dividing 16, or K = 32 or 64, with SH2 <= 256 runs the per-block
+        # backward kernel (the launch plan's rule)
+        rows = (16 % w.K == 0 or w.K in (32, 64)) and w.SH2 <= 256
+        bname = "gscan_bwd_rows_kernel" if rows else "gscan_bwd_kernel"
         kname, kus, kbytes, kflops = bname, k_bwd, w.bwd_bytes(), w.bwd_flops()
     else:
         kname, kus, kbytes, kflops = "gscan_fwd_kernel", k_fwd, w.fwd_bytes(), w.fwd_flops()

@@ -128,6 +128,37 @@ def _prep(h_history, h_s2, W_A, W_B, W_C, K):
     return dev, code, B, K, SH2, D
 
 
+def _check_f32(t, shape, dev, name):
+    """A caller-supplied float32 tensor the library reads or writes: the exact
+    shape, contiguous, on the inputs' device (the kernels index it by shape
+    alone, so anything else would be read or written out of bounds)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device != dev:
+        raise ValueError(f"{name} must be a tensor on {dev}")
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}; "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def _check_outs(out, shapes, dev, name="out"):
+    if not isinstance(out, (tuple, list)) or len(out) != len(shapes):
+        raise ValueError(f"{name} must hold {len(shapes)} tensors")
+    for i, (t, shp) in enumerate(zip(out, shapes)):
+        _check_f32(t, shp, dev, f"{name}[{i}]")
+
+
+def _check_workspace(ws, need, dev):
+    """A caller workspace: a contiguous uint8 GPU tensor on `dev` of at least
+    `need` bytes (the library also checks size and alignment)."""
+    import torch
+    if not isinstance(ws, torch.Tensor) or ws.device != dev:
+        raise ValueError(f"workspace must be a tensor on {dev}")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, needs {need}")
+
+
 def forward(h_history, h_s2, W_A, W_B, W_C, K: int, a_shift: float = 0.0, out=None,
             stream=None):
     """context[B, D] (float32) = C * x_K for every (sample, state)."""
@@ -135,8 +166,8 @@ def forward(h_history, h_s2, W_A, W_B, W_C, K: int, a_shift: float = 0.0, out=No
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
     if out is None:
         out = torch.empty((B, D), dtype=torch.float32, device=dev)
-    elif out.shape != (B, D) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, D] tensor")
+    else:
+        _check_f32(out, (B, D), dev, "out")
     _check(lib().gscan_forward_ex(
         h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
         W_C.data_ptr(), B, K, SH2, D, out.data_ptr(), code, float(a_shift),
@@ -158,14 +189,16 @@ def backward(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: float =
     """
     import torch
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
-    if (not d_context.is_cuda or d_context.dtype != torch.float32
-            or tuple(d_context.shape) != (B, D) or not d_context.is_contiguous()):
-        raise ValueError("d_context must be a contiguous float32 [B, D] GPU tensor")
+    _check_f32(d_context, (B, D), dev, "d_context")
     if out is None:
         out = tuple(torch.empty((SH2, D), dtype=torch.float32, device=dev) for _ in range(3))
+    else:
+        _check_outs(out, [(SH2, D)] * 3, dev)
     ws_bytes = int(lib().gscan_backward_workspace_bytes(B, K, SH2, D, code))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_workspace(workspace, ws_bytes, dev)
     _check(lib().gscan_backward_ex(
         h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
         W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), out[0].data_ptr(),
@@ -186,16 +219,18 @@ def backward_full(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: fl
     [SH2, D] x 3, [B*K, SH2] and [B, SH2].  `out` may hold those five tensors."""
     import torch
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
-    if (not d_context.is_cuda or d_context.dtype != torch.float32
-            or tuple(d_context.shape) != (B, D) or not d_context.is_contiguous()):
-        raise ValueError("d_context must be a contiguous float32 [B, D] GPU tensor")
+    _check_f32(d_context, (B, D), dev, "d_context")
     if out is None:
         out = tuple(torch.empty((SH2, D), dtype=torch.float32, device=dev) for _ in range(3)) + (
             torch.empty((B * K, SH2), dtype=torch.float32, device=dev),
             torch.empty((B, SH2), dtype=torch.float32, device=dev))
+    else:
+        _check_outs(out, [(SH2, D)] * 3 + [(B * K, SH2), (B, SH2)], dev)
     ws_bytes = int(lib().gscan_backward_full_workspace_bytes(B, K, SH2, D, code))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_workspace(workspace, ws_bytes, dev)
     _check(lib().gscan_backward_full_ex(
         h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
         W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), out[0].data_ptr(),
@@ -207,6 +242,10 @@ def backward_full(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: fl
 def prepare_backward_full(h_history, h_s2, W_A, W_B, W_C, K, d_context, out, workspace,
                           a_shift=0.0, stream=None):
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    _check_f32(d_context, (B, D), dev, "d_context")
+    _check_outs(out, [(SH2, D)] * 3 + [(B * K, SH2), (B, SH2)], dev)
+    _check_workspace(workspace, int(lib().gscan_backward_full_workspace_bytes(B, K, SH2, D, code)),
+                     dev)
     args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
             W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), out[0].data_ptr(),
             out[1].data_ptr(), out[2].data_ptr(), out[3].data_ptr(), out[4].data_ptr(), code,
@@ -226,9 +265,13 @@ def bias_grad_reduce(grad, out=None, workspace=None, stream=None):
     rows, cols = grad.shape
     if out is None:
         out = torch.empty(cols, dtype=torch.float32, device=grad.device)
+    else:
+        _check_f32(out, (cols,), grad.device, "out")
+    n = int(lib().gscan_bias_grad_reduce_workspace_bytes(rows, cols))
     if workspace is None:
-        n = int(lib().gscan_bias_grad_reduce_workspace_bytes(rows, cols))
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=grad.device)
+    else:
+        _check_workspace(workspace, n, grad.device)
     _check(lib().gscan_bias_grad_reduce(grad.data_ptr() if rows else None, rows, cols,
                                         out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                         _stream_handle(stream, grad.device)))
@@ -236,7 +279,13 @@ def bias_grad_reduce(grad, out=None, workspace=None, stream=None):
 
 
 def prepare_bias_grad_reduce(grad, out, workspace, stream=None):
+    _check_f32(grad, tuple(grad.shape), grad.device, "grad")
+    if grad.dim() != 2:
+        raise ValueError("grad must be [rows, cols]")
     rows, cols = grad.shape
+    _check_f32(out, (cols,), grad.device, "out")
+    _check_workspace(workspace, int(lib().gscan_bias_grad_reduce_workspace_bytes(rows, cols)),
+                     grad.device)
     args = (grad.data_ptr(), rows, cols, out.data_ptr(), workspace.data_ptr(), workspace.numel(),
             _stream_handle(stream, grad.device))
     return Prepared(lib().gscan_bias_grad_reduce, args, (grad, out, workspace))
@@ -247,6 +296,8 @@ def backward_partials(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, workspa
     """Phase 1 of the backward: per-workgroup weight-gradient partials into
     `workspace` (a uint8 device tensor of at least backward_workspace_bytes())."""
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    _check_f32(d_context, (B, D), dev, "d_context")
+    _check_workspace(workspace, int(lib().gscan_backward_workspace_bytes(B, K, SH2, D, code)), dev)
     _check(lib().gscan_backward_partials(
         h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(), W_C.data_ptr(),
         B, K, SH2, D, d_context.data_ptr(), code, float(a_shift), workspace.data_ptr(),
@@ -256,6 +307,10 @@ def backward_partials(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, workspa
 def backward_reduce(workspace, B: int, K: int, SH2: int, D: int, out, bf16: bool = False,
                     stream=None):
     """Phase 2 of the backward: fixed-order sum of the partials into out = (dW_A, dW_B, dW_C)."""
+    code = GSCAN_BF16 if bf16 else GSCAN_F32
+    _check_workspace(workspace, int(lib().gscan_backward_workspace_bytes(B, K, SH2, D, code)),
+                     workspace.device)
+    _check_outs(out, [(SH2, D)] * 3, workspace.device)
     _check(lib().gscan_backward_reduce(
         workspace.data_ptr(), workspace.numel(), B, K, SH2, D,
         GSCAN_BF16 if bf16 else GSCAN_F32, out[0].data_ptr(), out[1].data_ptr(),
@@ -280,6 +335,7 @@ class Prepared:
 
 def prepare_forward(h_history, h_s2, W_A, W_B, W_C, K, out, a_shift=0.0, stream=None):
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    _check_f32(out, (B, D), dev, "out")
     args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
             W_C.data_ptr(), B, K, SH2, D, out.data_ptr(), code, ctypes.c_float(a_shift),
             _stream_handle(stream, dev))
@@ -289,6 +345,9 @@ def prepare_forward(h_history, h_s2, W_A, W_B, W_C, K, out, a_shift=0.0, stream=
 def prepare_backward(h_history, h_s2, W_A, W_B, W_C, K, d_context, out, workspace,
                      a_shift=0.0, stream=None):
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    _check_f32(d_context, (B, D), dev, "d_context")
+    _check_outs(out, [(SH2, D)] * 3, dev)
+    _check_workspace(workspace, int(lib().gscan_backward_workspace_bytes(B, K, SH2, D, code)), dev)
     args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
             W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), out[0].data_ptr(),
             out[1].data_ptr(), out[2].data_ptr(), code, ctypes.c_float(a_shift),
@@ -300,6 +359,8 @@ def prepare_backward(h_history, h_s2, W_A, W_B, W_C, K, d_context, out, workspac
 def prepare_backward_partials(h_history, h_s2, W_A, W_B, W_C, K, d_context, workspace,
                               a_shift=0.0, stream=None):
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    _check_f32(d_context, (B, D), dev, "d_context")
+    _check_workspace(workspace, int(lib().gscan_backward_workspace_bytes(B, K, SH2, D, code)), dev)
     args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
             W_C.data_ptr(), B, K, SH2, D, d_context.data_ptr(), code, ctypes.c_float(a_shift),
             workspace.data_ptr(), workspace.numel(), _stream_handle(stream, dev))
@@ -308,6 +369,10 @@ def prepare_backward_partials(h_history, h_s2, W_A, W_B, W_C, K, d_context, work
 
 
 def prepare_backward_reduce(workspace, B, K, SH2, D, out, bf16=False, stream=None):
+    code = GSCAN_BF16 if bf16 else GSCAN_F32
+    _check_workspace(workspace, int(lib().gscan_backward_workspace_bytes(B, K, SH2, D, code)),
+                     workspace.device)
+    _check_outs(out, [(SH2, D)] * 3, workspace.device)
     args = (workspace.data_ptr(), workspace.numel(), B, K, SH2, D,
             GSCAN_BF16 if bf16 else GSCAN_F32, out[0].data_ptr(), out[1].data_ptr(),
             out[2].data_ptr(), _stream_handle(stream, workspace.device))

@@ -30,6 +30,15 @@ bool aligned16(const void *p)
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// hipGetLastError() returns and resets the calling thread's most recent HIP
+// error, whichever call raised it.  Each entry point clears it once its
+// arguments have passed validation and before it enqueues anything, so the
+// checks after its own launches report only its own failures.
+void clear_stale_error()
+{
+    (void)hipGetLastError();
+}
+
 int check_common(const void *hh, const void *hs2, const float *WA, const float *WB,
                  const float *WC, int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype,
                  gscan::Plan *plan)
@@ -114,6 +123,7 @@ int gscan_forward_ex(const void *h_history, const void *h_s2, const float *W_A, 
     if (!context_out) return fail(GSCAN_ERR_INVALID_ARGUMENT, "null context_out");
     if (!aligned16(context_out))
         return fail(GSCAN_ERR_MISALIGNED, "context_out must be 16-byte aligned");
+    clear_stale_error();
     hipError_t e = gscan::launch_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
                                          context_out, stream);
     if (e != hipSuccess)
@@ -151,6 +161,7 @@ int gscan_backward_ex(const void *h_history, const void *h_s2, const float *W_A,
     if ((st = check_outputs(dW_A, dW_B, dW_C)) != GSCAN_OK) return st;
     if (workspace && (st = check_workspace(workspace, workspace_bytes, plan)) != GSCAN_OK)
         return st;
+    clear_stale_error();
     void *ws = workspace;
     if (!ws) {
         hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, stream);
@@ -205,6 +216,7 @@ int gscan_backward_full_ex(const void *h_history, const void *h_s2, const float 
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
             return fail(GSCAN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
     }
+    clear_stale_error();
     void *ws = workspace;
     if (!ws) {
         hipError_t e = hipMallocAsync(&ws, lay.bytes, stream);
@@ -260,6 +272,7 @@ int gscan_bias_grad_reduce(const float *grad, int64_t rows, int64_t cols, float 
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
             return fail(GSCAN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
     }
+    clear_stale_error();
     void *ws = workspace;
     if (!ws) {
         hipError_t e = hipMallocAsync(&ws, need, stream);
@@ -289,6 +302,7 @@ int gscan_backward_partials(const void *h_history, const void *h_s2, const float
                             (int)in_dtype, &plan);
     if (st != GSCAN_OK) return st;
     if ((st = check_workspace(workspace, workspace_bytes, plan)) != GSCAN_OK) return st;
+    clear_stale_error();
     hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
                                                    d_context, static_cast<float *>(workspace),
                                                    nullptr, nullptr, stream);
@@ -312,6 +326,7 @@ int gscan_backward_reduce(const void *workspace, size_t workspace_bytes, int64_t
     int st;
     if ((st = check_workspace(workspace, workspace_bytes, plan)) != GSCAN_OK) return st;
     if ((st = check_outputs(dW_A, dW_B, dW_C)) != GSCAN_OK) return st;
+    clear_stale_error();
     hipError_t e = gscan::launch_backward_reduce(plan, static_cast<const float *>(workspace), dW_A,
                                                  dW_B, dW_C, stream);
     if (e != hipSuccess)

@@ -62,23 +62,29 @@ gscan_colsum_partial_kernel(const float *__restrict__ grad, int64_t rows, int64_
     }
 }
 
+// workgroup b takes columns b, b + gridDim.x, ... (the grid is capped, so any
+// column count the validation admits is covered)
 __global__ void __launch_bounds__(kColThreads)
 gscan_colsum_final_kernel(const double *__restrict__ part, int64_t nparts, int64_t cols,
                           float *__restrict__ out)
 {
     __shared__ double red[kColThreads];
     const int t = threadIdx.x;
-    const int64_t j = blockIdx.x;
-    double s = 0.0;
-    for (int64_t p = t; p < nparts; p += kColThreads) s += part[p * cols + j];
-    red[t] = s;
-    __syncthreads();
-    for (int w = kColThreads / 2; w > 0; w >>= 1) {
-        if (t < w) red[t] += red[t + w];
+    for (int64_t j = blockIdx.x; j < cols; j += gridDim.x) {
+        double s = 0.0;
+        for (int64_t p = t; p < nparts; p += kColThreads) s += part[p * cols + j];
+        red[t] = s;
         __syncthreads();
+        for (int w = kColThreads / 2; w > 0; w >>= 1) {
+            if (t < w) red[t] += red[t + w];
+            __syncthreads();
+        }
+        if (t == 0) out[j] = (float)red[0];
+        __syncthreads();  // red is rewritten for the next column
     }
-    if (t == 0) out[j] = (float)red[0];
 }
+
+constexpr int64_t kFinalMaxGrid = 65536;
 
 // rows per phase-1 workgroup: about 4096 elements each, at most 1024 groups
 int64_t colsum_blocks(int64_t rows, int64_t cols, int64_t *rows_per_block)
@@ -113,7 +119,8 @@ hipError_t launch_colsum(const float *grad, int64_t rows, int64_t cols, float *o
                        grad, rows, cols, rpb, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gscan_colsum_final_kernel, dim3((unsigned)cols), dim3(kColThreads), 0, st,
+    const int64_t fg = cols < kFinalMaxGrid ? cols : kFinalMaxGrid;
+    hipLaunchKernelGGL(gscan_colsum_final_kernel, dim3((unsigned)fg), dim3(kColThreads), 0, st,
                        part, g, cols, out);
     return hipGetLastError();
 }

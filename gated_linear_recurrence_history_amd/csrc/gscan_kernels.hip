@@ -22,7 +22,8 @@
 // nearest even), keeping hi*hi + hi*lo + lo*hi and accumulating in fp32.
 // The dropped terms are below 2^-16 of each product.  bf16 inputs are exact
 // in hi, so their lo term vanishes and is skipped.  dW_C, the only contraction
-// over samples rather than rows, uses fp32 MFMA.
+// over samples rather than rows, uses the same split products in the
+// per-block backward kernel and fp32 MFMA (16x16x4) in the general one.
 //
 // Work decomposition
 //   workgroup = 4 wavefronts = one "group" of 16 samples x one 16-state slice

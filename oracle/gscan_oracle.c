@@ -122,6 +122,9 @@ void oracle_forward(const double *h_history, const double *h_s2,
  *     dB_t = lam
  *     dA_t = lam * x_t * g_t * (1 - g_t)
  *     lam  = g_t * lam         (now dL/dx_t)
+ *   The logistic derivative g(1 - g) is formed as sigmoid(a) * sigmoid(-a):
+ *   the same number, but 1 - g taken as sigmoid(-a) keeps its relative
+ *   precision when the gate saturates towards 1 (1.0 - g would cancel).
  * Step 3: dW_A[i,s] = sum_rows h[r,i] dA[r,s]; dW_B likewise with dB;
  *   dW_C[i,s] = sum_b h_s2[b,i] dC[b,s].
  */
@@ -146,6 +149,7 @@ void oracle_backward(const double *h_history, const double *h_s2,
         double *Bv = (double *)malloc(sizeof(double) * D);
         double *xs = (double *)malloc(sizeof(double) * (K + 1) * D); /* x_0..x_K */
         double *gs = (double *)malloc(sizeof(double) * K * D);       /* g_0..g_{K-1} */
+        double *gc = (double *)malloc(sizeof(double) * K * D);       /* 1 - g_t */
         double *lam = (double *)malloc(sizeof(double) * D);
         double *dA = (double *)malloc(sizeof(double) * D);
         double *dB = (double *)malloc(sizeof(double) * D);
@@ -165,6 +169,7 @@ void oracle_backward(const double *h_history, const double *h_s2,
                 for (s = 0; s < D; ++s) {
                     const double g = sigmoid(Av[s] + a_shift);
                     gs[t * D + s] = g;
+                    gc[t * D + s] = sigmoid(-(Av[s] + a_shift));
                     xs[(t + 1) * D + s] = g * xs[t * D + s] + Bv[s];
                 }
             }
@@ -178,7 +183,7 @@ void oracle_backward(const double *h_history, const double *h_s2,
                 for (s = 0; s < D; ++s) {
                     const double g = gs[t * D + s];
                     dB[s] = lam[s];
-                    dA[s] = lam[s] * xs[t * D + s] * g * (1.0 - g);
+                    dA[s] = lam[s] * xs[t * D + s] * g * gc[t * D + s];
                     lam[s] = g * lam[s];
                 }
                 /* Step 3 rows of h_history^T @ d_gate and h_history^T @ d_x */
@@ -198,6 +203,7 @@ void oracle_backward(const double *h_history, const double *h_s2,
         free(Bv);
         free(xs);
         free(gs);
+        free(gc);
         free(lam);
         free(dA);
         free(dB);
@@ -240,6 +246,7 @@ void oracle_backward_inputs(const double *h_history, const double *h_s2,
         double *Bv = (double *)malloc(sizeof(double) * D);
         double *xs = (double *)malloc(sizeof(double) * (K + 1) * D); /* x_0..x_K */
         double *gs = (double *)malloc(sizeof(double) * K * D);       /* g_0..g_{K-1} */
+        double *gc = (double *)malloc(sizeof(double) * K * D);       /* 1 - g_t */
         double *adj = (double *)malloc(sizeof(double) * D); /* dL/dx_{t+1} */
         double *dA = (double *)malloc(sizeof(double) * D);
         double *dB = (double *)malloc(sizeof(double) * D);
@@ -259,6 +266,7 @@ void oracle_backward_inputs(const double *h_history, const double *h_s2,
                 for (s = 0; s < D; ++s) {
                     const double gt = sigmoid(a_shift + Av[s]);
                     gs[t * D + s] = gt;
+                    gc[t * D + s] = sigmoid(-(a_shift + Av[s]));
                     xs[(t + 1) * D + s] = gt * xs[t * D + s] + Bv[s];
                 }
             }
@@ -272,7 +280,7 @@ void oracle_backward_inputs(const double *h_history, const double *h_s2,
                 for (s = 0; s < D; ++s) {
                     const double gt = gs[t * D + s];
                     dB[s] = adj[s];
-                    dA[s] = adj[s] * xs[t * D + s] * gt * (1.0 - gt);
+                    dA[s] = adj[s] * xs[t * D + s] * gt * gc[t * D + s];
                     adj[s] = gt * adj[s];
                 }
                 /* row t of d_gate @ W_A^T + d_x @ W_B^T */
@@ -296,6 +304,7 @@ void oracle_backward_inputs(const double *h_history, const double *h_s2,
         free(Bv);
         free(xs);
         free(gs);
+        free(gc);
         free(adj);
         free(dA);
         free(dB);

@@ -19,9 +19,11 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "gscan_oracle.c")
 
 MUTANTS = {
     "forward_recurrence_wrong": ("x[s] = g * x[s] + Bv[s];", "x[s] = x[s] + g * Bv[s];"),
-    "dA_drops_state": ("dA[s] = lam[s] * xs[t * D + s] * g * (1.0 - g);",
-                       "dA[s] = lam[s] * g * (1.0 - g);"),
-    "dA_wrong_sign": ("g * (1.0 - g);", "g * (1.0 + g);"),
+    "dA_drops_state": ("dA[s] = lam[s] * xs[t * D + s] * g * gc[t * D + s];",
+                       "dA[s] = lam[s] * g * gc[t * D + s];"),
+    # the complement 1 - g taken with the wrong sign of the argument (g * g)
+    "dA_wrong_sign": ("gc[t * D + s] = sigmoid(-(Av[s] + a_shift));",
+                      "gc[t * D + s] = sigmoid(Av[s] + a_shift);"),
     "reverse_drops_gate": ("lam[s] = g * lam[s];", "lam[s] = lam[s];"),
     "dC_literal_upstream": ("dC[s] = d_context[b * D + s] * xs[K * D + s];",
                             "dC[s] = d_context[b * D + s];"),
@@ -43,8 +45,13 @@ MUTANTS = {
     "dh_rows_reversed": ("double *out = d_h_history + (b * K + t) * SH2;",
                          "double *out = d_h_history + (b * K + (K - 1 - t)) * SH2;"),
     "dh_reverse_drops_gate": ("adj[s] = gt * adj[s];", "adj[s] = adj[s];"),
-    "dh_dA_drops_state": ("dA[s] = adj[s] * xs[t * D + s] * gt * (1.0 - gt);",
-                          "dA[s] = adj[s] * gt * (1.0 - gt);"),
+    "dh_dA_drops_state": ("dA[s] = adj[s] * xs[t * D + s] * gt * gc[t * D + s];",
+                          "dA[s] = adj[s] * gt * gc[t * D + s];"),
+    "dh_complement_wrong_sign": ("gc[t * D + s] = sigmoid(-(a_shift + Av[s]));",
+                                 "gc[t * D + s] = sigmoid(a_shift + Av[s]);"),
+    # the complement by subtraction: loses its precision at saturated gates
+    "dA_complement_by_subtraction": ("gc[t * D + s] = sigmoid(-(Av[s] + a_shift));",
+                                     "gc[t * D + s] = 1.0 - g;"),
     "dhs2_literal_upstream": ("dC[s] = xs[K * D + s] * d_context[b * D + s];",
                               "dC[s] = d_context[b * D + s];"),
     "dhs2_wrong_weight": ("v += dC[s] * W_C[ii * D + s];", "v += dC[s] * W_B[ii * D + s];"),
@@ -61,6 +68,7 @@ MUTANTS = {
 def _pins():
     yield lambda: pins.test_gate_zero_closed_form(5, 8, 64, 16)
     yield lambda: pins.test_constant_gate_geometric_sum(0.9, 8)
+    yield lambda: pins.test_k2_closed_form_saturated_gates(30.0)
     yield lambda: pins.test_k1_reduces_to_c_times_b(2.0)
     yield lambda: pins.test_explicit_solution_of_recurrence(2.0, 3, 5, 20, 4)
     yield lambda: pins.test_euler_homogeneity(2.0)

@@ -57,6 +57,34 @@ def test_gate_zero_closed_form(B, K, SH2, D):
     assert _rel(dWC, x["h_s2"].T @ (dc * Bl)) < 1e-12
 
 
+@pytest.mark.parametrize("a_shift", [30.0, -30.0, 0.0])
+def test_k2_closed_form_saturated_gates(a_shift):
+    # K = 2: x_1 = B_0 and x_2 = g_1 B_0 + B_1 (g_0 multiplies x_0 = 0), so
+    # dL/dA_1 = d * C * B_0 * sigma'(a_1) and dL/dA_0 = 0.  The logistic
+    # derivative is written here as e^{-a} / (1 + e^{-a})^2, which keeps full
+    # relative precision at a = +30 where the gate is 1 - 1e-13; an oracle
+    # forming 1 - g by subtraction would be off by about 1e-3 there.
+    B, SH2, D = 6, 24, 5
+    K = 2
+    x = _inputs(B, K, SH2, D, 13)
+    Cv = x["h_s2"] @ x["W_C"]
+    A = x["h_history"] @ x["W_A"] + a_shift
+    Bv = x["h_history"] @ x["W_B"]
+    r0, r1 = np.arange(B) * K, np.arange(B) * K + 1
+    a1 = A[r1]
+    e = np.exp(-a1)
+    dsig = e / (1.0 + e) ** 2
+    g1 = 1.0 / (1.0 + e)
+    dc = x["d_context"]
+    dA1 = dc * Cv * Bv[r0] * dsig
+    dWA, dWB, dWC = _bwd(x, K, a_shift)
+    assert _rel(dWA, x["h_history"][r1].T @ dA1) < 1e-12
+    lam = dc * Cv
+    expect_B = x["h_history"][r1].T @ lam + x["h_history"][r0].T @ (lam * g1)
+    assert _rel(dWB, expect_B) < 1e-12
+    assert _rel(dWC, x["h_s2"].T @ (dc * (g1 * Bv[r0] + Bv[r1]))) < 1e-12
+
+
 @pytest.mark.parametrize("g", [0.5, 0.9])
 @pytest.mark.parametrize("K", [1, 4, 8])
 def test_constant_gate_geometric_sum(g, K):

@@ -4,16 +4,28 @@
 One step = one forward pass and one backward pass (both phases) over one
 batch of the headline workload B=8192, K=8, SH2=256, D=16 (fp32), with all
 inputs already resident in HBM.  Steps rotate over several distinct input
-sets (together larger than the 256 MB Infinity Cache) so the timed traffic
-is real HBM traffic.  Prints one JSON line.
+sets (together larger than the 256 MB Infinity Cache), so no step finds the
+data of an earlier step in that cache.  Within a step the backward reads
+the set its forward has just streamed, and part of those reads may be
+served by the Infinity Cache (the natural forward-then-backward pattern on
+one batch); `no_reuse` times the same work with the backward on a set the
+forward did not touch.  Prints one JSON line.
 
 Fields beyond the headline value:
   hbm_frac          algorithmic bytes per step / step time / 8 TB/s
+  read_ceiling_GBs  a measured read ceiling: a read-only stream of 1 GiB
+                    (two 1 GiB halves read alternately, so no read is served
+                    by the Infinity Cache), bytes over time, median of 8
+  frac_of_read_ceiling  algorithmic bytes per step / step time / that ceiling
+  no_reuse          the step with the backward on input set i+2 while the
+                    forward runs on set i (the backward's set was last read
+                    six passes, 432 MiB, earlier): time per step, samples/s,
+                    fraction of 8 TB/s and of the read ceiling
   step_us           p10 / p50 / p90 of single-step times (an event pair
                     around each step, measured after the timed region)
-  copy_GBs          a measured streaming ceiling for context: bytes read
-                    plus written by a 512 MiB device-to-device copy over its
-                    time (median of 5)
+  copy_GBs          a streaming figure for context: bytes read plus written
+                    by a 512 MiB device-to-device copy over its time (median
+                    of 5)
   kernels_us        average duration of each kernel: HIP events on the
                     launch stream around a run of back-to-back launches of
                     that kernel alone
@@ -40,9 +52,10 @@ Fields beyond the headline value:
                     the input gradients on a small sample
 
 The matrix products run on bf16 MFMA with fp32 operands split into a high
-and a low bf16 part (three products per fp32 product), so the MFMA time of a
-pass is at most 3 x its fp32 flops / 2.5 PFLOP/s -- well under its HBM time:
-every pass is bounded by HBM bandwidth.
+and a low bf16 part (three products per fp32 product, fp32 accumulation;
+`dtype` says so), so the MFMA time of a pass is at most 3 x its fp32 flops /
+2.5 PFLOP/s -- well under its HBM time: every pass is bounded by HBM
+bandwidth.
 """
 import argparse
 import json
@@ -269,6 +282,42 @@ def bias_grad(args, stream, reps, rows=524288, cols=3):
                        "sample": f"the same shape, {passes} calls in {t:.2f} s"}}
 
 
+def read_ceiling(stream, nbytes=1 << 30, reps=8):
+    """GB/s of a read-only stream over `nbytes` (libgscan_calib.so), two
+    buffers of that size read alternately (each exceeds the Infinity Cache,
+    so every read comes from HBM); median over `reps` reads."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_linear_recurrence_history_amd",
+                                   "libgscan_calib.so"))
+    lib.gscan_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    lib.gscan_calib_read.restype = ctypes.c_int
+    lib.gscan_calib_read_grid.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    bufs = [torch.full((nbytes // 4,), float(i + 1), dtype=torch.float32, device=dev)
+            for i in range(2)]
+    sink = torch.empty(lib.gscan_calib_read_grid(), dtype=torch.int32, device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    times = []
+    for i in range(reps + 2):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rc = lib.gscan_calib_read(bufs[i % 2].data_ptr(), nbytes, sink.data_ptr(), sh)
+        b.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"gscan_calib_read failed: {rc}")
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    del bufs
+    torch.cuda.empty_cache()
+    return nbytes / float(np.median(times[2:])) / 1e9
+
+
 def traffic_record(kernel, workload):
     """HBM bytes per launch measured by rocprofv3 for this exact kernel source, or None."""
     from gated_linear_recurrence_history_amd import rocprof_summary as rs
@@ -345,6 +394,25 @@ def main():
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
 
+    # ---- the same steps with the backward on a set the forward did not
+    # touch: set i + 2 was last read six passes (6 x 72 MiB) earlier
+    # (needs five sets or more; with fewer the figure is left out)
+    nr_ms = None
+    if n >= 5:
+        for i in range(2 * n):
+            fwd[i % n]()
+            bwd[(i + 2) % n]()
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record(stream)
+        for i in range(args.steps):
+            fwd[i % n]()
+            bwd[(i + 2) % n]()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        nr_ms = r0.elapsed_time(r1) / args.steps
+
     # ---- per-kernel durations: each kernel launched back to back on the same
     # stream (rotating the input sets), HIP events around the whole run
     reps = max(20, min(args.steps, 200))
@@ -396,9 +464,12 @@ def main():
     copy_gbs = 2 * cb / float(np.median(ctimes[1:])) / 1e9
     del csrc, cdst
 
+    rd_gbs = read_ceiling(stream)
+
     step_bytes = w.fwd_bytes() + w.bwd_bytes()
     value = w.B / (ms_step * 1e-3)
     hbm_frac = step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
 
     # dominant kernel against HBM (its MFMA time, 3 bf16 products per fp32
     # product at the bf16 peak, is far below its HBM time)
@@ -416,6 +487,7 @@ def main():
     rec = traffic_record(kname, w.name)
     roof = {"bound": "hbm" if t_hbm_us >= t_mfma_us else "mfma", "achieved": round(ach, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+            "frac_of_read_ceiling": round(ach / rd_gbs, 4),
             "traffic": rec["traffic_bytes"] if rec else None,
             "kernel": kname, "avg_us": round(kus, 3), "algorithmic_bytes": kbytes,
             "hbm_floor_us": round(t_hbm_us, 3), "mfma_floor_us": round(t_mfma_us, 3)}
@@ -431,11 +503,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if w.in_dtype == "f32" else "bf16-in/f32",
+        "dtype": ("f32 (bf16x3 split products, fp32 accumulate)" if w.in_dtype == "f32"
+                  else "bf16 in, f32 weights (bf16 MFMA products, fp32 accumulate)"),
         "data": "synthetic",
         "config": dict(w.describe(), input_sets=args.sets),
         "hbm_frac": round(hbm_frac, 4),
-        "hbm_GBs_fwd_bwd": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_GBs_fwd_bwd": round(step_gbs, 1),
+        "read_ceiling_GBs": round(rd_gbs, 1),
+        "frac_of_read_ceiling": round(step_gbs / rd_gbs, 4),
+        "no_reuse": None if nr_ms is None else {
+            "ms_per_step": round(nr_ms, 5),
+            "samples_per_s": round(w.B / (nr_ms * 1e-3), 1),
+            "hbm_frac": round(step_bytes / (nr_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "frac_of_read_ceiling": round(step_bytes / (nr_ms * 1e-3) / 1e9 / rd_gbs, 4),
+            "backward_set_offset": 2},
         "step_us": step_us,
         "copy_GBs": round(copy_gbs, 1),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 5),

@@ -6,9 +6,10 @@ kernels behind a C ABI, declared in include/gscan.h); `forward` and
 ctypes wrappers over it.  There is no CPU fallback.
 """
 from .binding import (forward, backward, backward_full, backward_workspace_bytes,  # noqa: F401
-                      backward_full_workspace_bytes, bias_grad_reduce, library_path, GScanError)
+                      backward_full_workspace_bytes, backward_partials, backward_reduce,
+                      bias_grad_reduce, library_path, GScanError)
 from . import workloads  # noqa: F401
 
 __all__ = ["forward", "backward", "backward_full", "backward_workspace_bytes",
-           "backward_full_workspace_bytes", "bias_grad_reduce", "library_path", "GScanError",
-           "workloads"]
+           "backward_full_workspace_bytes", "backward_partials", "backward_reduce",
+           "bias_grad_reduce", "library_path", "GScanError", "workloads"]

@@ -2,6 +2,7 @@
 
   libgscan.so        HIP kernels + C ABI (hipcc, gfx950 only)
   libgscan_synth.so  seeded input generator (gcc + OpenMP)
+  libgscan_calib.so  read-only stream used by the benchmark as its ceiling
 """
 from __future__ import annotations
 
@@ -68,9 +69,24 @@ def build_hip(verbose: bool = False) -> str:
     return out
 
 
+def build_calib(verbose: bool = False) -> str:
+    """libgscan_calib.so: the read-only stream the benchmark measures as its
+    bandwidth ceiling (no part of the scan)."""
+    out = os.path.join(PKG, "libgscan_calib.so")
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", os.path.join(CSRC, "gscan_calib.hip"),
+           "-o", tmp]
+    _run(cmd, verbose)
+    os.replace(tmp, out)
+    return out
+
+
 def build_all(verbose: bool = False) -> None:
     build_synth(verbose)
     build_hip(verbose)
+    build_calib(verbose)
 
 
 if __name__ == "__main__":

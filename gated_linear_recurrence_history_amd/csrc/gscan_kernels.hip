@@ -292,6 +292,24 @@ __device__ __forceinline__ float sigmoid(float a)
     return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
+// The gate and its complement 1 - g = sigmoid(-a) from one exponential: with
+// e = exp(-a), g = 1/(1+e) and 1 - g = e*g.  The product form serves a > 0,
+// where 1 - g would cancel as the gate saturates towards 1 (the logistic
+// derivative g(1-g) keeps its relative precision there); for a <= 0,
+// g <= 1/2 and 1 - g is exact to rounding, and e*g would be inf*0 once e
+// overflows.
+struct Gate {
+    float g, gc;
+};
+
+__device__ __forceinline__ Gate gate_of(float a)
+{
+    const float e = __expf(-a);
+    const float g = __builtin_amdgcn_rcpf(1.0f + e);
+    Gate r = {g, a > 0.f ? e * g : 1.0f - g};
+    return r;
+}
+
 // ------------------------------------------------------------ row bookkeeping
 // A lane's four rows in a block are base + 4*(l/16) + j, j = 0..3, with base
 // uniform across the wavefront.  (sample, step) = divmod(row, K) is formed
@@ -1146,15 +1164,17 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             RowPos bp = {0, 0};
             if constexpr (!ALIGNED) bp = base_pos(lr0, K);
             Aff fm[4], rm[4];
-            float gate[4];
+            float gate[4], gcom[4];
             Aff F = aff_id();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = lr0 + 4 * kg + j;
                 const RowPos rp = rowpos(bp, r, j);
                 const int bl = rp.bl, t = rp.t;
-                const float gt = sigmoid(aA[0][j] + a_shift);
+                const Gate gg = gate_of(aA[0][j] + a_shift);
+                const float gt = gg.g;
                 gate[j] = gt;
+                gcom[j] = gg.gc;
                 if (r >= ce) {
                     fm[j] = aff_id();
                     rm[j] = aff_id();
@@ -1247,7 +1267,7 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                 const bool v = r < ce;
                 const float gt = gate[j];
                 dB4[j] = v ? m_in : 0.f;
-                dA4[j] = v ? m_in * xbef[j] * (gt * (1.f - gt)) : 0.f;
+                dA4[j] = v ? m_in * xbef[j] * (gt * gcom[j]) : 0.f;
                 m_in = apply(rm[j], m_in);
             }
             dab[buf][wave][0][lane] = dA4;
@@ -1598,15 +1618,16 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         // groups.  Rows past the group's end are identity steps with zero
         // gradients.  Resets are selects, never multiplications, so a
         // non-finite value stays inside its sample.
-        float gate[4], beta[4];
+        float gate[4], gcom[4], beta[4];
         int tj[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = lr0 + 4 * kg + j;
             tj[j] = r & (K - 1);
             const bool v = r < ce;
-            const float gt = sigmoid(aA[j] + a_shift);
-            gate[j] = v ? gt : 1.f;
+            const Gate gg = gate_of(aA[j] + a_shift);
+            gate[j] = v ? gg.g : 1.f;
+            gcom[j] = gg.gc;
             beta[j] = v ? aB[j] : 0.f;
         }
         // LDS values of the walks, read up front (clamped rows; used only
@@ -1726,7 +1747,7 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             const bool v = r < ce;
             const float gt = gate[j];
             dB4[j] = v ? m_in : 0.f;
-            dA4[j] = v ? m_in * xbef[j] * (gt * (1.f - gt)) : 0.f;
+            dA4[j] = v ? m_in * xbef[j] * (gt * gcom[j]) : 0.f;
             // a sample starts at row j (K < 4): the row before ends the previous one
             if (j > 0) m_in = tj[j] == 0 ? lprev[j] : gt * m_in;
         }
@@ -1946,11 +1967,11 @@ gscan_adjoint_kernel(float *__restrict__ ab, float *__restrict__ cv,
     cv[i] = d * x;  // dL/dC = d_context * x_K
     for (int64_t t = K - 1; t >= 0; --t) {
         float *row = base + t * 2 * D;
-        const float g = sigmoid(row[0] + a_shift);
+        const Gate gg = gate_of(row[0] + a_shift);
         const float xt = row[D];
-        row[D] = lam;                      // dL/dBv_t
-        row[0] = lam * xt * (g * (1.f - g));  // dL/dA_t
-        lam = g * lam;
+        row[D] = lam;                           // dL/dBv_t
+        row[0] = lam * xt * (gg.g * gg.gc);     // dL/dA_t
+        lam = gg.g * lam;
     }
 }
 

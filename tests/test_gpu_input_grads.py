@@ -67,10 +67,12 @@ def test_input_grad_parity(case):
 
 
 @pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
-def test_input_grad_full_size_sampled(name):
+def test_input_grad_full_size(name):
     """Each named workload at full size in the benchmark's launch
-    configuration: the rows of sampled samples against the oracle on those
-    samples (a sample's input gradients depend on that sample alone), and
+    configuration: every element of d_h_history and d_h_s2 against the
+    oracle, except for the wide workload (2^21 rows of 512: hours of host
+    time for the fp64 oracle), where the rows of 64 sampled samples are
+    compared (a sample's input gradients depend on that sample alone); and
     <h_s2, dL/dh_s2> = L over the whole batch (L is linear in h_s2)."""
     w = wl.BY_NAME[name]
     tol = wl.tolerance(w)
@@ -80,22 +82,32 @@ def test_input_grad_full_size_sampled(name):
     out = gs.backward_full(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K,
                            t["d_context"], w.a_shift)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(4242)
-    n_s = min(w.B, 64 if w.K * w.SH2 <= 64 * 256 else 16)
-    samples = np.sort(np.concatenate([[0, w.B - 1], rng.choice(np.arange(1, w.B - 1), n_s - 2,
-                                                                 replace=False)]))
-    rows = (samples[:, None] * w.K + np.arange(w.K)[None, :]).reshape(-1)
-    got_dh = out[3][torch.from_numpy(rows).to(out[3].device)].cpu().numpy()
-    got_dhs = out[4].cpu().numpy()
-    sub = oracle.sample_rows(x, w.K, samples)
-    ref_dh, ref_dhs = oracle.backward_inputs(sub["h_history"], sub["h_s2"], sub["W_A"],
-                                             sub["W_B"], sub["W_C"], w.K, sub["d_context"],
-                                             w.a_shift)
-    e1, e2 = ctx_err(got_dh, ref_dh), ctx_err(got_dhs[samples], ref_dhs)
-    print(f"  sampled d_h_history {e1:.2e} d_h_s2 {e2:.2e} over {len(samples)} samples",
-          flush=True)
-    assert e1 <= min(tol, 1e-4) and e2 <= min(tol, 1e-4)
     assert bool(torch.isfinite(out[3]).all())
+    got_dhs = out[4].cpu().numpy()
+    if w.name != "wide_fp32":
+        got_dh = out[3].cpu().numpy()
+        ref_dh, ref_dhs = oracle.backward_inputs(x["h_history"], x["h_s2"], x["W_A"], x["W_B"],
+                                                 x["W_C"], w.K, x["d_context"], w.a_shift)
+        e1, e2 = ctx_err(got_dh, ref_dh), ctx_err(got_dhs, ref_dhs)
+        del got_dh, ref_dh
+        print(f"  d_h_history {e1:.2e} d_h_s2 {e2:.2e} (all rows)", flush=True)
+    else:
+        rng = np.random.default_rng(4242)
+        n_s = 64
+        samples = np.sort(np.concatenate([[0, w.B - 1],
+                                          rng.choice(np.arange(1, w.B - 1), n_s - 2,
+                                                     replace=False)]))
+        rows = (samples[:, None] * w.K + np.arange(w.K)[None, :]).reshape(-1)
+        got_dh = out[3][torch.from_numpy(rows).to(out[3].device)].cpu().numpy()
+        sub = oracle.sample_rows(x, w.K, samples)
+        ref_dh, ref_dhs = oracle.backward_inputs(sub["h_history"], sub["h_s2"], sub["W_A"],
+                                                 sub["W_B"], sub["W_C"], w.K, sub["d_context"],
+                                                 w.a_shift)
+        e1, e2 = ctx_err(got_dh, ref_dh), ctx_err(got_dhs[samples], ref_dhs)
+        print(f"  sampled d_h_history {e1:.2e} d_h_s2 {e2:.2e} over {len(samples)} samples",
+              flush=True)
+    assert e1 <= min(tol, 1e-4) and e2 <= min(tol, 1e-4)
+    del out
     ctx = gpu_forward(t, w.K, w.a_shift).astype(np.float64)
     L = float(np.sum(x["d_context"].astype(np.float64) * ctx))
     prod = oracle.widen(x["h_s2"]) * got_dhs.astype(np.float64)

@@ -2,10 +2,11 @@
 
 Small and ragged shapes compare every output element; the five named
 workloads run at full size in the same launch configuration the benchmark
-times, checked element-wise where the oracle can afford it and otherwise on
-sampled outputs (forward: a spread of samples; backward: an upstream
-gradient supported on sampled samples, whose exact weight gradients are the
-oracle's on those samples alone) plus properties that hold at any size.
+times and are compared element by element too (context and the weight
+gradients of the seeded upstream gradient); the wide workload's oracle
+outputs are read from a stored file written by a committed script that
+calls only the oracle.  Saturated gates, the gate-zero closed form and the
+two backward phases called separately are covered at full batch.
 
 Tolerances (from the method's stated targets): context max |err| <=
 tol*(1+|ref|), each dW relative L2 <= tol, tol = 1e-4 (fp32 inputs) or
@@ -13,17 +14,20 @@ tol*(1+|ref|), each dW relative L2 <= tol, tol = 1e-4 (fp32 inputs) or
 fp32, so bf16 cases are additionally held to 1e-4 against the oracle that
 uses the same rounded values.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
 
+import gated_linear_recurrence_history_amd as gs
 import oracle
 from gated_linear_recurrence_history_amd import synth, workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from tests.gpu_util import (ctx_err, device_inputs, gpu_backward, gpu_forward, rel_l2,  # noqa: E402
-                            to_dev, workload)
+from tests.gpu_util import (DEV, ctx_err, device_inputs, gpu_backward, gpu_forward,  # noqa: E402
+                            rel_l2, to_dev, workload)
 
 SMALL = [
     # B, K, SH2, D, dtype, a_shift
@@ -97,13 +101,6 @@ def test_parity_small(case):
     _check(x, w, ctx, dW, ref_ctx, ref_dW)
 
 
-def _spread(n_total, n, seed):
-    rng = np.random.default_rng(seed)
-    s = set(rng.choice(n_total, size=n - 2, replace=False).tolist())
-    s.update({0, n_total - 1})
-    return np.array(sorted(s), dtype=np.int64)
-
-
 def _euler(x, dWB, dWC, ctx, tol):
     """L = sum d*ctx equals <W_B, dW_B> and <W_C, dW_C> (1-homogeneity), to the
     slack the parity tolerances allow."""
@@ -116,8 +113,42 @@ def _euler(x, dWB, dWC, ctx, tol):
         assert abs(ip - L) <= slack, (ip, L, slack)
 
 
+def _wide_golden():
+    """The stored oracle outputs of the wide workload (written by
+    tests/golden/make_wide_reference.py, which calls only the oracle and the
+    seeded generator)."""
+    import importlib.util
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "make_wide_reference.py")
+    spec = importlib.util.spec_from_file_location("make_wide_reference", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _full_reference(w, x):
+    """Oracle context and dW for the whole workload: computed here, or, for
+    the wide workload (minutes of host time), read from the stored oracle
+    outputs after checking they belong to exactly these inputs."""
+    if w.name == "wide_fp32":
+        mod = _wide_golden()
+        ref = np.load(mod.OUT, allow_pickle=False)
+        assert str(ref["inputs_sha256"]) == mod.input_digest(x), "stale wide reference"
+        return (ref["context"].astype(np.float64),
+                (ref["dW_A"], ref["dW_B"], ref["dW_C"]))
+    ref_ctx = oracle.forward(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], w.K,
+                             w.a_shift)
+    ref_dW = oracle.backward(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], w.K,
+                             x["d_context"], w.a_shift)
+    return ref_ctx, ref_dW
+
+
 @pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
 def test_parity_full_size(name):
+    """Every named workload at full size, in the launch configuration the
+    benchmark times, against the oracle element by element: all of context
+    and all of dW_A, dW_B, dW_C for the seeded upstream gradient (the weight
+    gradients accumulate every one of the B*K rows)."""
     w = wl.BY_NAME[name]
     tol = wl.tolerance(w)
     print(f"case full {w.name} B={w.B} K={w.K} SH2={w.SH2} D={w.D} {w.in_dtype}", flush=True)
@@ -125,37 +156,96 @@ def test_parity_full_size(name):
     t = device_inputs(x)
     ctx = gpu_forward(t, w.K, w.a_shift)
     dW = gpu_backward(t, w.K, w.a_shift)
+    del t
+    torch.cuda.empty_cache()
     assert np.all(np.isfinite(ctx)) and all(np.all(np.isfinite(g)) for g in dW)
-    if w.B * w.K * w.SH2 <= 8192 * 8 * 256:
-        # the oracle takes the whole workload
-        ref_ctx = oracle.forward(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], w.K,
-                                 w.a_shift)
-        ref_dW = oracle.backward(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], w.K,
-                                 x["d_context"], w.a_shift)
-        _check(x, w, ctx, dW, ref_ctx, ref_dW, tol=min(tol, 1e-4))
-    else:
-        # forward on a spread of samples
-        n_s = {"longK_fp32": 96, "bigbatch_bf16": 512, "wide_fp32": 24}.get(w.name, 64)
-        sidx = _spread(w.B, n_s, 11)
-        xs = oracle.sample_rows(x, w.K, sidx)
-        ref_ctx = oracle.forward(xs["h_history"], xs["h_s2"], xs["W_A"], xs["W_B"], xs["W_C"],
-                                 w.K, w.a_shift)
-        ce = ctx_err(ctx[sidx], ref_ctx)
-        print(f"  sampled ctx err {ce:.2e} over {len(sidx)} samples", flush=True)
-        assert ce <= min(tol, 1e-4)
-        # backward with the upstream gradient on sampled samples only
-        bidx = _spread(w.B, max(8, n_s // 2), 12)
-        dmask = np.zeros_like(x["d_context"])
-        dmask[bidx] = x["d_context"][bidx]
-        dWm = gpu_backward(t, w.K, w.a_shift, to_dev(dmask))
-        xb = oracle.sample_rows(x, w.K, bidx)
-        ref_dW = oracle.backward(xb["h_history"], xb["h_s2"], xb["W_A"], xb["W_B"], xb["W_C"],
-                                 w.K, xb["d_context"], w.a_shift)
-        ge = [rel_l2(g, r) for g, r in zip(dWm, ref_dW)]
-        print(f"  sampled dW err {['%.2e' % e for e in ge]} over {len(bidx)} samples", flush=True)
-        assert max(ge) <= min(tol, 1e-4)
-    # properties on the dense run
+    ref_ctx, ref_dW = _full_reference(w, x)
+    # bf16 inputs are widened exactly on both sides: the fp32 bar applies
+    _check(x, w, ctx, dW, ref_ctx, ref_dW, tol=min(tol, 1e-4))
     _euler(x, dW[1], dW[2], ctx.astype(np.float64), tol)
+
+
+@pytest.mark.parametrize("a_shift", [30.0, -30.0])
+def test_saturated_gates_full_batch(a_shift):
+    """Gates saturated at 1 - 1e-13 (+30) or 1e-13 (-30) over the headline
+    batch: dL/dA then carries the logistic derivative at 1e-13, which must
+    keep its relative precision (1 - g is not formed by subtraction)."""
+    w = wl.HEADLINE
+    print(f"case saturated {w.name} a_shift={a_shift}", flush=True)
+    x = synth.make_inputs(w)
+    t = device_inputs(x)
+    ctx = gpu_forward(t, w.K, a_shift)
+    dW = gpu_backward(t, w.K, a_shift)
+    ref_ctx = oracle.forward(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], w.K,
+                             a_shift)
+    ref_dW = oracle.backward(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], w.K,
+                             x["d_context"], a_shift)
+    ge = [rel_l2(g, r) for g, r in zip(dW, ref_dW)]
+    ce = ctx_err(ctx, ref_ctx)
+    print(f"  ctx {ce:.2e} dW {['%.2e' % e for e in ge]}", flush=True)
+    assert max(ge) <= 1e-4
+    # With every gate at 1 the state is the plain sum of the K projections,
+    # so their rounding errors add instead of decaying with the gates: each
+    # split product carries about 2^-17 relative error per operand, which
+    # puts the worst of the 131072 context values near 1.2e-4 (1 + |ref|)
+    # at K = 8.  The bar for this saturated edge case is 2e-4; the named
+    # workloads keep 1e-4.
+    assert ce <= (2e-4 if a_shift > 0 else 1e-4)
+
+
+@pytest.mark.parametrize("name", ["prod_fp32", "longK_fp32"])
+def test_gate_zero_closed_form_full_batch(name):
+    """a_shift = -1e4 makes every gate exactly 0 (in fp32 and fp64), so
+    context = C * Bv_{K-1}, dW_A = 0 exactly, dW_B = H_{K-1}^T (d * C) and
+    dW_C = h_s2^T (d * Bv_{K-1}), written here with numpy from the inputs."""
+    w = wl.BY_NAME[name]
+    a_shift = -1.0e4
+    print(f"case gate zero {w.name}", flush=True)
+    x = synth.make_inputs(w)
+    t = device_inputs(x)
+    ctx = gpu_forward(t, w.K, a_shift)
+    dWA, dWB, dWC = gpu_backward(t, w.K, a_shift)
+    h = x["h_history"].astype(np.float64)
+    last = h[np.arange(w.B) * w.K + w.K - 1]
+    Cv = x["h_s2"].astype(np.float64) @ x["W_C"].astype(np.float64)
+    Bl = last @ x["W_B"].astype(np.float64)
+    d = x["d_context"].astype(np.float64)
+    assert ctx_err(ctx, Cv * Bl) <= 1e-4
+    assert np.all(dWA == 0.0)
+    assert rel_l2(dWB, last.T @ (d * Cv)) <= 1e-4
+    assert rel_l2(dWC, x["h_s2"].astype(np.float64).T @ (d * Bl)) <= 1e-4
+
+
+@pytest.mark.parametrize("case", [
+    (8192, 8, 256, 16, "f32", 0.0),     # the headline: per-block backward kernel
+    (777, 5, 192, 32, "f32", 0.5),      # general backward kernel, ragged batch
+    (300, 8, 512, 64, "bf16", -1.0),    # SH2 above the per-block kernel's range
+], ids=lambda c: "B%d_K%d_S%d_D%d_%s_a%g" % c)
+def test_partials_then_reduce(case):
+    """The two exported phases called separately (phase 1 into a caller
+    workspace, then phase 2) give bitwise the one-call backward, and meet
+    the oracle."""
+    B, K, SH2, D, dt, a = case
+    w = workload(B, K, SH2, D, dt, a, seed=31)
+    print(f"case partials+reduce {w.name}", flush=True)
+    x = synth.make_inputs(w)
+    t = device_inputs(x)
+    ws = torch.empty(gs.backward_workspace_bytes(B, K, SH2, D, dt == "bf16"), dtype=torch.uint8,
+                     device=DEV)
+    gs.backward_partials(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], K,
+                         t["d_context"], ws, a)
+    out = tuple(torch.full((SH2, D), float("nan"), device=DEV) for _ in range(3))
+    gs.backward_reduce(ws, B, K, SH2, D, out, dt == "bf16")
+    torch.cuda.synchronize()
+    two = tuple(o.cpu().numpy() for o in out)
+    one = gpu_backward(t, K, a)
+    for p, q in zip(two, one):
+        assert np.array_equal(p, q)
+    ref_dW = oracle.backward(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], K,
+                             x["d_context"], a)
+    ge = [rel_l2(g, r) for g, r in zip(two, ref_dW)]
+    print(f"  dW {['%.2e' % e for e in ge]}", flush=True)
+    assert max(ge) <= 1e-4
 
 
 def test_linearity_in_upstream_gradient_full_size():

@@ -50,6 +50,9 @@ def lib():
         L.gscan_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp,
                                         ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.gscan_backward_ex.restype = ctypes.c_int
+        L.gscan_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp,
+                                             vp, ctypes.c_int, f32, vp]
+        L.gscan_backward_noalloc.restype = ctypes.c_int
         L.gscan_backward_partials.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp,
                                               ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.gscan_backward_partials.restype = ctypes.c_int

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "gscan.h"
 #include "gscan_internal.h"
@@ -105,6 +106,41 @@ int check_workspace(const void *workspace, size_t workspace_bytes, const gscan::
                     workspace_bytes, plan.ws_bytes);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(GSCAN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    return GSCAN_OK;
+}
+
+// ------------------------------------------- static scratch (no allocation)
+// The weight-gradient partials of gscan_backward_noalloc live in this
+// file-scope device array instead of caller or runtime memory.  Its host-side
+// name is only a stand-in: host code uses the device address that
+// hipGetSymbolAddress returns, looked up once per device (with that device
+// current) and kept.  Each device holds its own copy for the life of the
+// process.
+static __device__ __align__(256) unsigned char scratch[GSCAN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`.
+int current_scratch(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GSCAN_ERR_HIP, "device index %d outside 0..%d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GSCAN_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s",
+                        dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return GSCAN_OK;
 }
 
@@ -331,6 +367,39 @@ int gscan_backward_reduce(const void *workspace, size_t workspace_bytes, int64_t
                                                  dW_B, dW_C, stream);
     if (e != hipSuccess)
         return fail(GSCAN_ERR_HIP, "backward phase 2 launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return GSCAN_OK;
+}
+
+int gscan_backward_noalloc(const void *h_history, const void *h_s2, const float *W_A,
+                           const float *W_B, const float *W_C, int64_t B, int64_t K, int64_t SH2,
+                           int64_t D, const float *d_context, float *dW_A, float *dW_B,
+                           float *dW_C, gscan_dtype_t in_dtype, float a_shift,
+                           hipStream_t stream)
+{
+    gscan::Plan plan;
+    int st = check_backward(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, d_context,
+                            (int)in_dtype, &plan);
+    if (st != GSCAN_OK) return st;
+    if ((st = check_outputs(dW_A, dW_B, dW_C)) != GSCAN_OK) return st;
+    if (plan.ws_bytes > (size_t)GSCAN_NOALLOC_SCRATCH_BYTES)
+        return fail(GSCAN_ERR_WORKSPACE_TOO_SMALL,
+                    "shape B=%lld K=%lld SH2=%lld D=%lld needs %zu bytes of partials, more than "
+                    "the %zu-byte static scratch of gscan_backward_noalloc (use "
+                    "gscan_backward_ex with a workspace)",
+                    (long long)B, (long long)K, (long long)SH2, (long long)D, plan.ws_bytes,
+                    (size_t)GSCAN_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = current_scratch(&ws)) != GSCAN_OK) return st;
+    clear_stale_error();
+    // phase 1 overwrites every partial it leaves for phase 2: nothing in the
+    // scratch needs to start at zero
+    float *part = static_cast<float *>(ws);
+    hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
+                                                   d_context, part, nullptr, nullptr, stream);
+    if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     g_last_error[0] = '\0';
     return GSCAN_OK;
 }

@@ -29,13 +29,15 @@
  *
  * Pointers: every array pointer is DEVICE memory owned by the caller,
  * 16-byte aligned.  Inputs are read only and must not overlap outputs.  The
- * library keeps no allocation between calls.
+ * library keeps no allocation between calls, apart from the static scratch
+ * array of gscan_backward_noalloc (below).
  *
  * Semantics: each call validates its arguments, enqueues its kernels on
  * `stream` and returns without synchronising; outputs are valid once the
  * stream reaches that point.  Outputs are overwritten, never accumulated
  * into.  Results are bitwise reproducible for identical inputs and shapes
- * (no floating-point atomics).  Calls are reentrant.
+ * (no floating-point atomics).  Calls are reentrant (gscan_backward_noalloc:
+ * see its note on overlapping calls).
  *
  * Errors: a non-zero return is one of the GSCAN_ERR_* codes below.  All
  * argument checks run before anything is enqueued: on a validation error
@@ -183,6 +185,34 @@ int gscan_bias_grad_reduce(const float *grad, int64_t rows, int64_t cols, float 
 
 /* Workspace bytes of gscan_bias_grad_reduce (0 for invalid sizes). */
 size_t gscan_bias_grad_reduce_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * Backward without any allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, kernels and result as
+ * gscan_backward_ex, with the weight-gradient partials kept in a static
+ * device array of GSCAN_NOALLOC_SCRATCH_BYTES bytes inside the library
+ * (one per GPU, held until the process ends) instead of a workspace.  It
+ * calls no allocating routine; the array's device address is looked up once
+ * per device (the device current at the call).
+ *
+ * Limit: shapes whose gscan_backward_workspace_bytes() exceeds
+ * GSCAN_NOALLOC_SCRATCH_BYTES are rejected with
+ * GSCAN_ERR_WORKSPACE_TOO_SMALL before anything is launched (all five
+ * named workloads but the widest fit).
+ * Concurrency: every call on one GPU uses that GPU's one array, so calls
+ * that overlap on a GPU (on different streams, or from different threads
+ * without ordering) race; calls ordered on one stream are safe.  The array
+ * keeps the last call's partials; nothing in it needs to start at zero.
+ * Other arguments, layouts and errors as for gscan_backward_ex.
+ */
+#define GSCAN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int gscan_backward_noalloc(const void *h_history, const void *h_s2,
+                           const float *W_A, const float *W_B, const float *W_C,
+                           int64_t B, int64_t K, int64_t SH2, int64_t D,
+                           const float *d_context, float *dW_A, float *dW_B, float *dW_C,
+                           gscan_dtype_t in_dtype, float a_shift, hipStream_t stream);
 
 /* Workspace bytes gscan_backward_ex needs for this shape (0 if unsupported). */
 size_t gscan_backward_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,

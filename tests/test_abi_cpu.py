@@ -148,3 +148,29 @@ def test_bias_grad_reduce_validation(lib, args, code):
     assert n >= 8 * c
     assert lib.gscan_bias_grad_reduce(g, r, c, o, FAKE, n - 8, None) == WS_SMALL
     assert lib.gscan_bias_grad_reduce_workspace_bytes(10, 0) == 0
+
+
+def _noalloc(lib, B=64, K=8, SH2=256, D=16, dctx=FAKE, dwa=FAKE, dtype=0, hh=FAKE):
+    return lib.gscan_backward_noalloc(hh, FAKE, FAKE, FAKE, FAKE, B, K, SH2, D, dctx, dwa, FAKE,
+                                      FAKE, dtype, 0.0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dctx=None), INVALID), (dict(dwa=None), INVALID), (dict(hh=None), INVALID),
+    (dict(D=17), UNSUPPORTED), (dict(dctx=FAKE + 4), MISALIGNED),
+    # the wide workload's 24 MiB of partials exceed the 16 MiB static scratch
+    (dict(B=8192, K=256, SH2=512, D=128), WS_SMALL),
+])
+def test_backward_noalloc_validation(lib, kw, code):
+    assert _noalloc(lib, **kw) == code
+    assert lib.gscan_last_error() != b""
+
+
+def test_backward_noalloc_limit_message(lib):
+    assert _noalloc(lib, B=8192, K=256, SH2=512, D=128) == WS_SMALL
+    assert b"static scratch" in lib.gscan_last_error()
+    # every other named workload fits the scratch
+    for cfg in wl.WORKLOADS:
+        dt = 1 if cfg.in_dtype == "bf16" else 0
+        need = lib.gscan_backward_workspace_bytes(cfg.B, cfg.K, cfg.SH2, cfg.D, dt)
+        assert (need <= (16 << 20)) == (cfg.name != "wide_fp32"), cfg.name

@@ -44,6 +44,9 @@ Fields beyond the headline value:
                     IQN shape [524288 x 3] (fp32, synthetic N(0, 9)): HIP-event
                     time per call, bytes read against 8 TB/s, and the
                     oracle's rate
+  enrich            the forward that adds the context into a [B, SH2]
+                    h_enriched (gscan_forward_enrich): time per call and
+                    over the plain forward
   input_grads       the backward that also returns the input gradients
                     (gscan_backward_full_ex): HIP-event time per call on the
                     same rotated inputs, its algorithmic bytes (the backward's
@@ -184,6 +187,38 @@ def input_grads(args, w, sets, stream, bwd_us, reps):
                        "cores": oracle.max_threads(),
                        "sample": f"first {ns} samples, fp64 input gradients, {passes} passes "
                                  f"in {t:.1f} s"}}
+
+
+def enrich(w, sets, stream, fwd_us, reps):
+    """gscan_forward_enrich per call (the context added into a [B, SH2]
+    h_enriched at column 0, no separate context output), HIP events, rotated
+    inputs; its time over the plain forward."""
+    import torch
+
+    from gated_linear_recurrence_history_amd import binding
+
+    dev = sets[0]["h_history"].device
+    he = torch.zeros((w.B, w.SH2), dtype=torch.float32, device=dev)
+    fns = [binding.prepare_forward_enrich(t["h_history"], t["h_s2"], t["W_A"], t["W_B"],
+                                          t["W_C"], w.K, he, 0, w.a_shift, stream) for t in sets]
+    n = len(fns)
+    for i in range(max(20, n)):
+        fns[i % n]()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(reps):
+        fns[i % n]()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    # the forward's reads, plus the h_enriched slice read and written
+    nbytes = w.fwd_bytes() - w.B * w.D * 4 + 2 * w.B * w.D * 4
+    return {"entry": "gscan_forward_enrich", "h_enriched": [w.B, w.SH2], "col_offset": 0,
+            "us_per_call": round(us, 3), "over_forward_us": round(us - fwd_us, 3),
+            "algorithmic_bytes": nbytes,
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def all_configs(stream):
@@ -526,6 +561,7 @@ def main():
     }
     if not args.no_input_grads:
         out["input_grads"] = input_grads(args, w, sets, stream, k_bwd + k_red, reps)
+    out["enrich"] = enrich(w, sets, stream, k_fwd, reps)
     if not args.no_bias_grad:
         out["bias_grad_reduce"] = bias_grad(args, stream, reps)
     if not args.no_configs:

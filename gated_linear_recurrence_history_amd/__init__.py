@@ -5,11 +5,12 @@ kernels behind a C ABI, declared in include/gscan.h); `forward` and
 `backward` (and `backward_full`, which adds the input gradients) are thin
 ctypes wrappers over it.  There is no CPU fallback.
 """
-from .binding import (forward, backward, backward_full, backward_workspace_bytes,  # noqa: F401
+from .binding import (forward, forward_enrich, backward, backward_full,  # noqa: F401
+                      backward_workspace_bytes,
                       backward_full_workspace_bytes, backward_partials, backward_reduce,
                       bias_grad_reduce, library_path, GScanError)
 from . import workloads  # noqa: F401
 
-__all__ = ["forward", "backward", "backward_full", "backward_workspace_bytes",
+__all__ = ["forward", "forward_enrich", "backward", "backward_full", "backward_workspace_bytes",
            "backward_full_workspace_bytes", "backward_partials", "backward_reduce",
            "bias_grad_reduce", "library_path", "GScanError", "workloads"]

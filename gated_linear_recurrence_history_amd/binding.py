@@ -50,6 +50,9 @@ def lib():
         L.gscan_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp,
                                         ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.gscan_backward_ex.restype = ctypes.c_int
+        L.gscan_forward_enrich.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, i64,
+                                           i64, ctypes.c_int, f32, vp]
+        L.gscan_forward_enrich.restype = ctypes.c_int
         L.gscan_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp,
                                              vp, ctypes.c_int, f32, vp]
         L.gscan_backward_noalloc.restype = ctypes.c_int
@@ -176,6 +179,43 @@ def forward(h_history, h_s2, W_A, W_B, W_C, K: int, a_shift: float = 0.0, out=No
         W_C.data_ptr(), B, K, SH2, D, out.data_ptr(), code, float(a_shift),
         _stream_handle(stream, dev)))
     return out
+
+
+def forward_enrich(h_history, h_s2, W_A, W_B, W_C, K: int, h_enriched, col_offset: int = 0,
+                   a_shift: float = 0.0, context_out=None, stream=None):
+    """Adds context[b, s] into h_enriched[b, col_offset + s] in place
+    (h_enriched: contiguous float32 [B, ld] on the inputs' device) and, if
+    `context_out` is given ([B, D] float32), writes the context there too.
+    Returns h_enriched."""
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    if h_enriched.dim() != 2:
+        raise ValueError("h_enriched must be [B, ld]")
+    _check_f32(h_enriched, (B, h_enriched.shape[1]), dev, "h_enriched")
+    ld = int(h_enriched.shape[1])
+    if not 0 <= int(col_offset) <= ld - D:
+        raise ValueError(f"col_offset {col_offset} outside 0..{ld - D} for h_enriched [B, {ld}]")
+    cptr = None
+    if context_out is not None:
+        _check_f32(context_out, (B, D), dev, "context_out")
+        cptr = context_out.data_ptr()
+    _check(lib().gscan_forward_enrich(
+        h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
+        W_C.data_ptr(), B, K, SH2, D, cptr, h_enriched.data_ptr(), ld, int(col_offset), code,
+        float(a_shift), _stream_handle(stream, dev)))
+    return h_enriched
+
+
+def prepare_forward_enrich(h_history, h_s2, W_A, W_B, W_C, K, h_enriched, col_offset=0,
+                           a_shift=0.0, stream=None):
+    dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
+    _check_f32(h_enriched, (B, h_enriched.shape[1]), dev, "h_enriched")
+    ld = int(h_enriched.shape[1])
+    if not 0 <= int(col_offset) <= ld - D:
+        raise ValueError("col_offset out of range")
+    args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
+            W_C.data_ptr(), B, K, SH2, D, None, h_enriched.data_ptr(), ld, int(col_offset), code,
+            ctypes.c_float(a_shift), _stream_handle(stream, dev))
+    return Prepared(lib().gscan_forward_enrich, args, (h_history, h_s2, W_A, W_B, W_C, h_enriched))
 
 
 def backward_workspace_bytes(B: int, K: int, SH2: int, D: int, bf16: bool = False) -> int:

@@ -160,8 +160,53 @@ int gscan_forward_ex(const void *h_history, const void *h_s2, const float *W_A, 
     if (!aligned16(context_out))
         return fail(GSCAN_ERR_MISALIGNED, "context_out must be 16-byte aligned");
     clear_stale_error();
-    hipError_t e = gscan::launch_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
-                                         context_out, stream);
+    gscan::CtxOut out;
+    out.ctx = context_out;
+    hipError_t e = gscan::launch_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out,
+                                         stream);
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return GSCAN_OK;
+}
+
+int gscan_forward_enrich(const void *h_history, const void *h_s2, const float *W_A,
+                         const float *W_B, const float *W_C, int64_t B, int64_t K, int64_t SH2,
+                         int64_t D, float *context_out, float *h_enriched, int64_t ld_enriched,
+                         int64_t col_offset, gscan_dtype_t in_dtype, float a_shift,
+                         hipStream_t stream)
+{
+    gscan::Plan plan;
+    int st = check_common(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, (int)in_dtype, &plan);
+    if (st != GSCAN_OK) return st;
+    if (!h_enriched) return fail(GSCAN_ERR_INVALID_ARGUMENT, "null h_enriched");
+    if (ld_enriched < D || col_offset < 0 || col_offset > ld_enriched - D)
+        return fail(GSCAN_ERR_INVALID_ARGUMENT,
+                    "need ld_enriched >= D and 0 <= col_offset <= ld_enriched - D (ld=%lld "
+                    "offset=%lld D=%lld)",
+                    (long long)ld_enriched, (long long)col_offset, (long long)D);
+    if (ld_enriched > (int64_t(1) << 40) / B)
+        return fail(GSCAN_ERR_UNSUPPORTED_SHAPE, "B x ld_enriched above 2^40");
+    if ((reinterpret_cast<uintptr_t>(h_enriched) & 3u) != 0)
+        return fail(GSCAN_ERR_MISALIGNED, "h_enriched must be 4-byte aligned");
+    if (context_out) {
+        if (!aligned16(context_out))
+            return fail(GSCAN_ERR_MISALIGNED, "context_out must be 16-byte aligned");
+        // the two outputs must not overlap (each element has one writer)
+        const uintptr_t c0 = reinterpret_cast<uintptr_t>(context_out);
+        const uintptr_t c1 = c0 + (uintptr_t)(B * D) * sizeof(float);
+        const uintptr_t e0 = reinterpret_cast<uintptr_t>(h_enriched);
+        const uintptr_t e1 = e0 + (uintptr_t)((B - 1) * ld_enriched + col_offset + D) * sizeof(float);
+        if (c0 < e1 && e0 < c1)
+            return fail(GSCAN_ERR_INVALID_ARGUMENT, "context_out overlaps h_enriched");
+    }
+    clear_stale_error();
+    gscan::CtxOut out;
+    out.ctx = context_out;
+    out.enr = h_enriched + col_offset;
+    out.ld = ld_enriched;
+    hipError_t e = gscan::launch_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out,
+                                         stream);
     if (e != hipSuccess)
         return fail(GSCAN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
     g_last_error[0] = '\0';

@@ -38,12 +38,21 @@ struct Plan {
     size_t ws_bytes = 0;    // weight-gradient partials: bwd_rows x 3 x SH2 x D floats
 };
 
+// Where the forward writes context[b][s]: the context output (null: not
+// written) and/or an add into row b of a caller buffer (null: none), whose
+// pointer already includes the column offset, with row pitch `ld` floats.
+struct CtxOut {
+    float *ctx = nullptr;
+    float *enr = nullptr;
+    int64_t ld = 0;
+};
+
 // Fills `p` for a validated shape.  Returns false if the shape is unsupported.
 bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p);
 
 hipError_t launch_forward(const Plan &p, const void *h_history, const void *h_s2,
                           const float *W_A, const float *W_B, const float *W_C,
-                          float a_shift, float *context, hipStream_t stream);
+                          float a_shift, const CtxOut &out, hipStream_t stream);
 
 // Phase 1: per-workgroup weight-gradient partials into `partials`.  When
 // `dab` / `dc` are not null they receive, for the input gradients, either

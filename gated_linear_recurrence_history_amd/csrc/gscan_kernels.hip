@@ -358,6 +358,17 @@ __device__ __forceinline__ int wave_id()
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
+// context[b][s] = v into the forward's outputs (each (b, s) has one writer,
+// so the add into the caller's row needs no atomic)
+__device__ __forceinline__ void put_context(const CtxOut &o, int64_t b, int D, int s, float v)
+{
+    if (o.ctx) o.ctx[b * D + s] = v;
+    if (o.enr) {
+        float *e = o.enr + b * o.ld + s;
+        *e = *e + v;
+    }
+}
+
 // --------------------------------------------------------------- weight slice
 // LDS image of [W_A | W_B | W_C][:, s0 .. s0+16) as bf16 hi/lo in MFMA
 // B-operand order: entry ((q*3 + w)*2 + part)*64 + lane holds rows
@@ -527,7 +538,7 @@ template <typename TIn, int NQ>
 __device__ __forceinline__ void fwd_block(const PBlk<TIn, NQ> &blk, const u4 *Wl, int base,
                                           int lr_end, int K, int D, int s0, int64_t b0,
                                           float a_shift, const float (*cvp)[16][16], int lane,
-                                          const LaneOff &lo, float &xc, float *__restrict__ ctx)
+                                          const LaneOff &lo, float &xc, const CtxOut &out)
 {
     const int kg = lane >> 4, ln = lane & 15;
     const RowPos bp = base_pos(base, K);
@@ -563,7 +574,7 @@ __device__ __forceinline__ void fwd_block(const PBlk<TIn, NQ> &blk, const u4 *Wl
         if (r < lr_end && rp.t == K - 1) {
             const int bl = rp.bl;
             const float cv = cvp[0][bl][ln] + cvp[1][bl][ln] + cvp[2][bl][ln] + cvp[3][bl][ln];
-            ctx[(b0 + bl) * D + s0 + ln] = cv * x;
+            put_context(out, b0 + bl, D, s0 + ln, cv * x);
         }
     }
     xc = apply(total, xc);
@@ -574,7 +585,7 @@ __global__ void __launch_bounds__(kThreads, NQ <= 8 ? 2 : 1)
 gscan_fwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                  const float *__restrict__ WA, const float *__restrict__ WB,
                  const float *__restrict__ WC, int64_t B, int K, int D, int slices,
-                 int64_t groups, float a_shift, float *__restrict__ ctx)
+                 int64_t groups, float a_shift, CtxOut out)
 {
     constexpr int SH2 = NQ * 32;
     __shared__ u4 Wl[NQ * 6 * kWave];
@@ -623,10 +634,10 @@ gscan_fwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     for (int base = lr_begin; base < lr_end; base += 2 * kBlockRows) {
         const int base1 = base + kBlockRows;
         b1buf.load(rowp(base1), kg);
-        fwd_block<TIn, NQ>(b0buf, Wl, base, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo, xc, ctx);
+        fwd_block<TIn, NQ>(b0buf, Wl, base, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo, xc, out);
         if (base1 >= lr_end) break;
         b0buf.load(rowp(base1 + kBlockRows), kg);
-        fwd_block<TIn, NQ>(b1buf, Wl, base1, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo, xc, ctx);
+        fwd_block<TIn, NQ>(b1buf, Wl, base1, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo, xc, out);
     }
 }
 
@@ -635,7 +646,7 @@ __global__ void __launch_bounds__(kThreads, NQ <= 8 ? 2 : 1)
 gscan_fwd_persist_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                  const float *__restrict__ WA, const float *__restrict__ WB,
                  const float *__restrict__ WC, int64_t B, int K, int D, int slices,
-                 int64_t groups, int64_t nrows, float a_shift, float *__restrict__ ctx)
+                 int64_t groups, int64_t nrows, float a_shift, CtxOut out)
 {
     constexpr int SH2 = NQ * 32;
     __shared__ u4 Wl[NQ * 6 * kWave];
@@ -695,11 +706,11 @@ gscan_fwd_persist_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2
                 const int base1 = base + kBlockRows;
                 b1buf.load(rowp(g, lr_end, base1), kg);
                 fwd_block<TIn, NQ>(b0buf, Wl, base, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo,
-                                   xc, ctx);
+                                   xc, out);
                 if (base1 >= lr_end) break;
                 b0buf.load(rowp(g, lr_end, base1 + kBlockRows), kg);
                 fwd_block<TIn, NQ>(b1buf, Wl, base1, lr_end, K, D, s0, b0, a_shift, cvp, lane, lo,
-                                   xc, ctx);
+                                   xc, out);
             }
         }
         g += nrows;
@@ -768,7 +779,7 @@ __global__ void __launch_bounds__(kThreadsM, 1)
 gscan_fwd_ms_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                     const float *__restrict__ WA, const float *__restrict__ WB,
                     const float *__restrict__ WC, int64_t B, int K, int D, int sgroups,
-                    int64_t groups, float a_shift, float *__restrict__ ctx)
+                    int64_t groups, float a_shift, CtxOut out)
 {
     constexpr int SH2 = NQ * 32;
     constexpr bool LO = PBlk<TIn, NQ>::kLo;
@@ -891,7 +902,7 @@ gscan_fwd_ms_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                 const int r = base + 4 * kg + j;
                 const RowPos rp = row_pos(bp, lo, j, K);
                 if (r < lr_end && rp.t == K - 1)
-                    ctx[(b0 + rp.bl) * D + s0 + 16 * s + ln] = cvs[team][s][rp.bl][ln] * x;
+                    put_context(out, b0 + rp.bl, D, s0 + 16 * s + ln, cvs[team][s][rp.bl][ln] * x);
             }
             xc[s] = apply(total, xc[s]);
         }
@@ -2054,7 +2065,7 @@ gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
 // ----------------------------------------------------------------- dispatch
 template <typename TIn, int NQ>
 hipError_t fwd_launch(const Plan &p, const void *hh, const void *hs2, const float *WA,
-                      const float *WB, const float *WC, float a_shift, float *ctx,
+                      const float *WB, const float *WC, float a_shift, const CtxOut &ctx,
                       hipStream_t st)
 {
     if (p.fwd_ms == 4) {
@@ -2126,7 +2137,7 @@ hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
 
 template <typename TIn>
 hipError_t fwd_by_nq(const Plan &p, const void *hh, const void *hs2, const float *WA,
-                     const float *WB, const float *WC, float a, float *ctx, hipStream_t st)
+                     const float *WB, const float *WC, float a, const CtxOut &ctx, hipStream_t st)
 {
     switch (p.nq) {
     case 2: return fwd_launch<TIn, 2>(p, hh, hs2, WA, WB, WC, a, ctx, st);
@@ -2212,7 +2223,7 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
 }
 
 hipError_t launch_forward(const Plan &p, const void *hh, const void *hs2, const float *WA,
-                          const float *WB, const float *WC, float a_shift, float *ctx,
+                          const float *WB, const float *WC, float a_shift, const CtxOut &ctx,
                           hipStream_t st)
 {
     if (p.dtype == 1) return fwd_by_nq<uint16_t>(p, hh, hs2, WA, WB, WC, a_shift, ctx, st);

@@ -80,6 +80,30 @@ int gscan_forward(const void *h_history, const void *h_s2,
                   float *context_out, hipStream_t stream);
 
 /*
+ * Forward with the context folded into a caller buffer (the step after the
+ * scan in the design spec: Forward Step 2 ends by accumulating the context
+ * into h_enriched, and Step 3 applies it element-wise).  Reading taken:
+ * h_enriched is a caller-owned fp32 row-major [B][ld_enriched] buffer (for
+ * example the enriched hidden state, of width SH2) and the context is added
+ * element-wise into the D columns starting at col_offset of each row:
+ *   h_enriched[b][col_offset + s] += context[b][s]
+ * Other columns are not touched.  Each element has exactly one writer, so no
+ * atomics are needed.  context_out may be NULL (then only h_enriched is
+ * updated) or a [B][D] buffer that must not overlap h_enriched.  h_enriched:
+ * device memory, 4-byte aligned; requires D <= ld_enriched and
+ * 0 <= col_offset <= ld_enriched - D (INVALID_ARGUMENT otherwise).  The add
+ * is a read-modify-write of h_enriched in stream order: a concurrent writer
+ * of the same rows on another stream races.  Other arguments and errors as
+ * for gscan_forward_ex.
+ */
+int gscan_forward_enrich(const void *h_history, const void *h_s2,
+                         const float *W_A, const float *W_B, const float *W_C,
+                         int64_t B, int64_t K, int64_t SH2, int64_t D,
+                         float *context_out, float *h_enriched, int64_t ld_enriched,
+                         int64_t col_offset, gscan_dtype_t in_dtype, float a_shift,
+                         hipStream_t stream);
+
+/*
  * Backward pass (Backward Steps 1-3): writes dW_A, dW_B, dW_C [SH2][D] for
  * the upstream gradient d_context[B][D].  Recomputes the forward from the
  * inputs; needs no saved activations.  Allocates its workspace stream-ordered

@@ -4,7 +4,8 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
 import this package.  The product path (the HIP library and its binding)
 never touches it.
 
-`forward` / `backward` / `backward_inputs` / `column_sums` widen every input exactly to float64 (float32 as is,
+`forward` / `forward_enrich` / `backward` / `backward_inputs` / `column_sums` widen every
+input exactly to float64 (float32 as is,
 bfloat16 given as raw uint16 bits by zero-extending the low mantissa) and
 call plain double-precision C loops (gscan_oracle.c).
 """
@@ -81,6 +82,23 @@ def forward(h_history, h_s2, W_A, W_B, W_C, K: int, a_shift: float = 0.0) -> np.
     _load().oracle_forward(h.ctypes.data, hs.ctypes.data, wa.ctypes.data, wb.ctypes.data,
                            wc.ctypes.data, B, K, SH2, D, float(a_shift), ctx.ctypes.data)
     return ctx
+
+
+def forward_enrich(h_history, h_s2, W_A, W_B, W_C, K: int, h_enriched, col_offset: int,
+                   a_shift: float = 0.0) -> np.ndarray:
+    """h_enriched [B, ld] (float64) with the context added element-wise into
+    columns col_offset .. col_offset + D - 1 of each row, other columns as
+    given.  The design spec's Forward Step 2 ends by accumulating the context
+    into h_enriched and its Step 3 applies it element-wise; the spec fixes
+    neither the buffer's width nor where the context lands, so the caller
+    names the row pitch and the column offset."""
+    ctx = forward(h_history, h_s2, W_A, W_B, W_C, K, a_shift)
+    out = widen(h_enriched).copy()
+    D = ctx.shape[1]
+    if out.ndim != 2 or out.shape[0] != ctx.shape[0] or not 0 <= col_offset <= out.shape[1] - D:
+        raise ValueError(f"h_enriched {out.shape} cannot take [B, {D}] at column {col_offset}")
+    out[:, col_offset:col_offset + D] += ctx
+    return out
 
 
 def backward(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: float = 0.0):

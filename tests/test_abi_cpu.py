@@ -174,3 +174,20 @@ def test_backward_noalloc_limit_message(lib):
         dt = 1 if cfg.in_dtype == "bf16" else 0
         need = lib.gscan_backward_workspace_bytes(cfg.B, cfg.K, cfg.SH2, cfg.D, dt)
         assert (need <= (16 << 20)) == (cfg.name != "wide_fp32"), cfg.name
+
+
+def _enrich(lib, B=64, K=8, SH2=256, D=16, ctx=None, he=FAKE, ld=256, off=0, dtype=0, hh=FAKE):
+    return lib.gscan_forward_enrich(hh, FAKE, FAKE, FAKE, FAKE, B, K, SH2, D, ctx, he, ld, off,
+                                    dtype, 0.0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(he=None), INVALID), (dict(hh=None), INVALID), (dict(ld=15), INVALID),
+    (dict(off=-1), INVALID), (dict(off=241), INVALID), (dict(ld=20, off=5), INVALID),
+    (dict(D=17), UNSUPPORTED), (dict(he=FAKE + 2), MISALIGNED), (dict(ctx=FAKE + 4), MISALIGNED),
+    # context_out inside h_enriched's rows: the outputs must not overlap
+    (dict(ctx=FAKE + 1024), INVALID),
+])
+def test_forward_enrich_validation(lib, kw, code):
+    assert _enrich(lib, **kw) == code
+    assert lib.gscan_last_error() != b""

@@ -335,3 +335,27 @@ def test_column_sums_against_correctly_rounded_sums():
     # columns are not mixed: permuting columns permutes the result
     perm = [2, 0, 1]
     assert np.array_equal(oracle.column_sums(np.ascontiguousarray(g[:, perm])), got[perm])
+
+
+@pytest.mark.parametrize("ld,off", [(16, 0), (40, 24), (37, 5)])
+def test_forward_enrich_adds_context_in_place(ld, off):
+    # the fold of the context into h_enriched (Forward Step 2's closing
+    # comment, Step 3): the D columns at the offset gain exactly the pinned
+    # forward's context, every other column is returned unchanged
+    B, K, SH2, D = 6, 3, 20, 16
+    x = _inputs(B, K, SH2, D, 21)
+    rng = np.random.default_rng(22)
+    h0 = rng.standard_normal((B, ld))
+    out = oracle.forward_enrich(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], K, h0,
+                                off, 0.5)
+    ctx = _fwd(x, K, 0.5)
+    keep = np.ones(ld, dtype=bool)
+    keep[off:off + D] = False
+    assert np.array_equal(out[:, keep], h0[:, keep])
+    assert np.array_equal(out[:, off:off + D], h0[:, off:off + D] + ctx)
+    z = oracle.forward_enrich(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], K,
+                              np.zeros((B, ld)), off, 0.5)
+    assert np.array_equal(z[:, off:off + D], ctx)
+    with pytest.raises(ValueError):
+        oracle.forward_enrich(x["h_history"], x["h_s2"], x["W_A"], x["W_B"], x["W_C"], K, h0,
+                              ld - D + 1, 0.5)

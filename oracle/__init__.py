@@ -4,8 +4,8 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
 import this package.  The product path (the HIP library and its binding)
 never touches it.
 
-`forward` / `forward_enrich` / `backward` / `backward_inputs` / `column_sums` widen every
-input exactly to float64 (float32 as is,
+`forward` / `forward_enrich` / `backward` / `backward_inputs` / `cifg_update` /
+`column_sums` widen every input exactly to float64 (float32 as is,
 bfloat16 given as raw uint16 bits by zero-extending the low mantissa) and
 call plain double-precision C loops (gscan_oracle.c).
 """
@@ -39,6 +39,8 @@ def _load():
         lib.oracle_backward_inputs.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
                                                ctypes.c_double, dp, dp, dp]
         lib.oracle_backward_inputs.restype = None
+        lib.oracle_cifg_update.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, dp]
+        lib.oracle_cifg_update.restype = None
         lib.oracle_column_sums.argtypes = [dp, i64, i64, dp]
         lib.oracle_column_sums.restype = None
         lib.oracle_max_threads.argtypes = []
@@ -128,6 +130,24 @@ def backward_inputs(h_history, h_s2, W_A, W_B, W_C, K: int, d_context, a_shift: 
                                    wb.ctypes.data, wc.ctypes.data, B, K, SH2, D, float(a_shift),
                                    dc.ctypes.data, dh.ctypes.data, dhs.ctypes.data)
     return dh, dhs
+
+
+def cifg_update(C, H, X, W_f, b_f) -> np.ndarray:
+    """The CIFG matrix-memory update of every sample, independent mode
+    (BURT-IMMA API reference, batched_cifg_update with shared_memory_mode
+    false; steps 1-4 of cifg_update): returns the updated C [B, d, d] in
+    float64.  H [B, d], X [B, d_input], W_f [d, d + d_input], b_f [d]."""
+    c, h, x, w, bf = (widen(a) for a in (C, H, X, W_f, b_f))
+    B, d = h.shape
+    d_input = x.shape[1] if x.ndim == 2 else 0
+    if (c.shape != (B, d, d) or x.shape != (B, d_input) or w.shape != (d, d + d_input)
+            or bf.shape != (d,)):
+        raise ValueError(f"shape mismatch: C {c.shape}, H {h.shape}, X {x.shape}, "
+                         f"W_f {w.shape}, b_f {bf.shape}")
+    out = np.empty_like(c)
+    _load().oracle_cifg_update(c.ctypes.data, h.ctypes.data, x.ctypes.data, w.ctypes.data,
+                               bf.ctypes.data, B, d, d_input, out.ctypes.data)
+    return out
 
 
 def column_sums(grad) -> np.ndarray:

@@ -331,3 +331,54 @@ void oracle_column_sums(const double *grad, int64_t rows, int64_t cols, double *
         out[j] = acc;
     }
 }
+
+/*
+ * CIFG matrix-memory update, independent mode (BURT-IMMA CUDA Kernel API
+ * Reference, section 2.3 batched_cifg_update with shared_memory_mode =
+ * false, which applies section 2.2 cifg_update to every sample):
+ *   concat = [h_b ; x_b]                          (length d_model + d_input)
+ *   f      = sigmoid(W_f @ concat + b_f)          (length d_model)
+ *   C_b[i, j] <- f[i] * C_b[i, j] + (1 - f[i]) * h_b[i] * h_b[j]
+ * (the candidate is the rank-1 outer product h h^T; f is broadcast along
+ * each row, i.e. over the columns j).  The optional spectral projection of
+ * step 5 is not part of this function.  C_in and C_out are [B][d][d],
+ * H [B][d], X [B][d_input], W_f [d][d + d_input], b_f [d].  1 - f is
+ * evaluated as sigmoid(-a) (no cancellation when the gate saturates).
+ */
+void oracle_cifg_update(const double *C_in, const double *H, const double *X,
+                        const double *W_f, const double *b_f, int64_t B, int64_t d,
+                        int64_t d_input, double *C_out)
+{
+    const int64_t L = d + d_input;
+    int64_t b;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (b = 0; b < B; ++b) {
+        double *concat = (double *)malloc(sizeof(double) * L);
+        double *f = (double *)malloc(sizeof(double) * d);
+        double *fc = (double *)malloc(sizeof(double) * d);
+        const double *h = H + b * d;
+        int64_t i, j, k;
+        /* step 1: concatenate */
+        for (k = 0; k < d; ++k)
+            concat[k] = h[k];
+        for (k = 0; k < d_input; ++k)
+            concat[d + k] = X[b * d_input + k];
+        /* step 2: forget gate */
+        for (i = 0; i < d; ++i) {
+            double a = b_f[i];
+            for (k = 0; k < L; ++k)
+                a += W_f[i * L + k] * concat[k];
+            f[i] = sigmoid(a);
+            fc[i] = sigmoid(-a);
+        }
+        /* steps 3-4: rank-1 candidate and the gated update */
+        for (i = 0; i < d; ++i)
+            for (j = 0; j < d; ++j) {
+                const int64_t e = (b * d + i) * d + j;
+                C_out[e] = f[i] * C_in[e] + fc[i] * (h[i] * h[j]);
+            }
+        free(concat);
+        free(f);
+        free(fc);
+    }
+}

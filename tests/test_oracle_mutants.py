@@ -56,6 +56,14 @@ MUTANTS = {
                               "dC[s] = d_context[b * D + s];"),
     "dhs2_wrong_weight": ("v += dC[s] * W_C[ii * D + s];", "v += dC[s] * W_B[ii * D + s];"),
     "dh_a_shift_ignored": ("sigmoid(a_shift + Av[s]);", "sigmoid(Av[s]);"),
+    # CIFG matrix-memory update
+    "cifg_concat_swapped": ("concat[k] = h[k];\n        for (k = 0; k < d_input; ++k)\n            concat[d + k] = X[b * d_input + k];",
+                            "concat[d_input + k] = h[k];\n        for (k = 0; k < d_input; ++k)\n            concat[k] = X[b * d_input + k];"),
+    "cifg_gate_per_column": ("C_out[e] = f[i] * C_in[e] + fc[i] * (h[i] * h[j]);",
+                             "C_out[e] = f[j] * C_in[e] + fc[j] * (h[i] * h[j]);"),
+    "cifg_candidate_h_x": ("fc[i] * (h[i] * h[j]);", "fc[i] * (h[i] * X[b * d_input + j % d_input]);"),
+    "cifg_no_bias": ("double a = b_f[i];", "double a = 0.0;"),
+    "cifg_complement_is_gate": ("fc[i] = sigmoid(-a);", "fc[i] = sigmoid(a);"),
     # bias-gradient reduction
     "colsum_transposed": ("acc += grad[r * cols + j];", "acc += grad[j * rows + r];"),
     "colsum_drops_last_row": ("for (r = 0; r < rows; ++r)\n            acc",
@@ -79,6 +87,13 @@ def _pins():
     yield lambda: pins.test_input_grad_k1_and_linearity()
     for a in (-3.0, 0.0, 2.0):
         yield lambda a=a: pins.test_input_grad_central_finite_differences(a)
+    from tests import test_oracle_cifg_pins as cp
+    yield lambda: cp.test_gate_one_keeps_memory(3, 8, 5)
+    yield lambda: cp.test_gate_zero_gives_outer_product(3, 8, 5)
+    yield lambda: cp.test_constant_gate(0.25)
+    yield cp.test_gate_is_per_row
+    yield cp.test_concat_order_h_then_x
+    yield cp.test_linear_in_memory_and_samples_independent
     yield pins.test_column_sums_exact_cases
     yield pins.test_column_sums_against_correctly_rounded_sums
 
@@ -96,7 +111,7 @@ def test_mutant_is_caught(name, tmp_path):
     real = oracle._load()
     mut = ctypes.CDLL(str(lib_path))
     for fn in ("oracle_forward", "oracle_backward", "oracle_backward_inputs", "oracle_column_sums",
-               "oracle_max_threads", "oracle_set_threads"):
+               "oracle_cifg_update", "oracle_max_threads", "oracle_set_threads"):
         getattr(mut, fn).argtypes = getattr(real, fn).argtypes
         getattr(mut, fn).restype = getattr(real, fn).restype
     caught = False

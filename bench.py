@@ -47,6 +47,10 @@ Fields beyond the headline value:
   enrich            the forward that adds the context into a [B, SH2]
                     h_enriched (gscan_forward_enrich): time per call and
                     over the plain forward
+  cifg              the CIFG matrix-memory update in independent mode
+                    (gscan_batched_cifg_update) on the page's batch 32,
+                    d_model 512 and on batch 256: time per call, bytes (C read
+                    and written once) against 8 TB/s, the oracle's time
   input_grads       the backward that also returns the input gradients
                     (gscan_backward_full_ex): HIP-event time per call on the
                     same rotated inputs, its algorithmic bytes (the backward's
@@ -219,6 +223,62 @@ def enrich(w, sets, stream, fwd_us, reps):
             "us_per_call": round(us, 3), "over_forward_us": round(us - fwd_us, 3),
             "algorithmic_bytes": nbytes,
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def cifg(stream, reps):
+    """gscan_batched_cifg_update (independent mode) on the page's shape
+    (batch 32, d_model 512, d_input 512) and on a batch of 256: HIP-event time
+    per call, rotating over memory sets larger than the Infinity Cache, its
+    algorithmic bytes (C read and written once) against 8 TB/s, and the
+    oracle's time per call on the page's shape."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from gated_linear_recurrence_history_amd import binding, synth, workloads as wl
+
+    dev = torch.device("cuda:0")
+    res = {}
+    for w in (wl.CIFG_PAGE, wl.CifgWorkload("cifg_b256", 256, 512, 512)):
+        x = synth.make_cifg_inputs(w)
+        per = w.B * w.d_model * w.d_model * 4
+        nsets = max(2, int(np.ceil(300e6 / per)))
+        Cs = [torch.from_numpy(x["C"]).to(dev) for _ in range(nsets)]
+        t = {k: torch.from_numpy(v).to(dev) for k, v in x.items() if k != "C"}
+        fns = [binding.prepare_batched_cifg_update(C, t["H"], t["X"], t["W_f"], t["b_f"], stream)
+               for C in Cs]
+        for i in range(2 * nsets):
+            fns[i % nsets]()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(reps):
+            fns[i % nsets]()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        nbytes = w.bytes()
+        res[w.name] = dict(w.describe(), us_per_call=round(us, 3), algorithmic_bytes=nbytes,
+                           GBs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                           hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           memory_sets=nsets)
+        del Cs, t, fns
+        torch.cuda.empty_cache()
+        if w is wl.CIFG_PAGE:
+            t0 = time.perf_counter()
+            passes = 0
+            while True:
+                oracle.cifg_update(x["C"], x["H"], x["X"], x["W_f"], x["b_f"])
+                passes += 1
+                if time.perf_counter() - t0 > 1.0:
+                    break
+            el = time.perf_counter() - t0
+            res[w.name]["oracle"] = {"us_per_call": round(el / passes * 1e6, 1),
+                                     "cores": oracle.max_threads(),
+                                     "sample": f"the same shape, {passes} calls in {el:.2f} s"}
+    res["entry"] = "gscan_batched_cifg_update"
+    return res
 
 
 def all_configs(stream):
@@ -562,6 +622,7 @@ def main():
     if not args.no_input_grads:
         out["input_grads"] = input_grads(args, w, sets, stream, k_bwd + k_red, reps)
     out["enrich"] = enrich(w, sets, stream, k_fwd, reps)
+    out["cifg"] = cifg(stream, reps)
     if not args.no_bias_grad:
         out["bias_grad_reduce"] = bias_grad(args, stream, reps)
     if not args.no_configs:

@@ -53,6 +53,8 @@ def lib():
         L.gscan_forward_enrich.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, i64,
                                            i64, ctypes.c_int, f32, vp]
         L.gscan_forward_enrich.restype = ctypes.c_int
+        L.gscan_batched_cifg_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        L.gscan_batched_cifg_update.restype = ctypes.c_int
         L.gscan_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp,
                                              vp, ctypes.c_int, f32, vp]
         L.gscan_backward_noalloc.restype = ctypes.c_int
@@ -216,6 +218,42 @@ def prepare_forward_enrich(h_history, h_s2, W_A, W_B, W_C, K, h_enriched, col_of
             W_C.data_ptr(), B, K, SH2, D, None, h_enriched.data_ptr(), ld, int(col_offset), code,
             ctypes.c_float(a_shift), _stream_handle(stream, dev))
     return Prepared(lib().gscan_forward_enrich, args, (h_history, h_s2, W_A, W_B, W_C, h_enriched))
+
+
+def batched_cifg_update(C_batch, H, X, W_f, b_f, stream=None):
+    """In-place CIFG matrix-memory update of every sample (independent mode):
+    C_batch [B, d, d] <- f * C_batch + (1 - f) * h h^T with
+    f = sigmoid(W_f [h; x] + b_f) per row.  All float32 contiguous GPU
+    tensors on one device; X is [B, d_input] (d_input may be 0).  Returns
+    C_batch."""
+    import torch
+    if not isinstance(C_batch, torch.Tensor) or not C_batch.is_cuda or C_batch.dim() != 3:
+        raise ValueError("C_batch must be a [B, d, d] GPU tensor")
+    dev = C_batch.device
+    B, d = int(C_batch.shape[0]), int(C_batch.shape[1])
+    _check_f32(C_batch, (B, d, d), dev, "C_batch")
+    _check_f32(H, (B, d), dev, "H")
+    if X.dim() != 2:
+        raise ValueError("X must be [B, d_input]")
+    din = int(X.shape[1])
+    _check_f32(X, (B, din), dev, "X")
+    _check_f32(W_f, (d, d + din), dev, "W_f")
+    _check_f32(b_f, (d,), dev, "b_f")
+    _check(lib().gscan_batched_cifg_update(
+        C_batch.data_ptr(), H.data_ptr(), X.data_ptr() if din else None, W_f.data_ptr(),
+        b_f.data_ptr(), B, d, din, _stream_handle(stream, dev)))
+    return C_batch
+
+
+def prepare_batched_cifg_update(C_batch, H, X, W_f, b_f, stream=None):
+    B, d, din = int(C_batch.shape[0]), int(C_batch.shape[1]), int(X.shape[1])
+    dev = C_batch.device
+    for t, shp, nm in ((C_batch, (B, d, d), "C_batch"), (H, (B, d), "H"), (X, (B, din), "X"),
+                       (W_f, (d, d + din), "W_f"), (b_f, (d,), "b_f")):
+        _check_f32(t, shp, dev, nm)
+    args = (C_batch.data_ptr(), H.data_ptr(), X.data_ptr() if din else None, W_f.data_ptr(),
+            b_f.data_ptr(), B, d, din, _stream_handle(stream, dev))
+    return Prepared(lib().gscan_batched_cifg_update, args, (C_batch, H, X, W_f, b_f))
 
 
 def backward_workspace_bytes(B: int, K: int, SH2: int, D: int, bf16: bool = False) -> int:

@@ -458,6 +458,45 @@ int gscan_backward(const void *h_history, const void *h_s2, const float *W_A, co
                              dW_C, GSCAN_F32, 0.0f, nullptr, 0, stream);
 }
 
+int gscan_batched_cifg_update(float *C_batch, const float *H, const float *X, const float *W_f,
+                              const float *b_f, int64_t B, int64_t d_model, int64_t d_input,
+                              hipStream_t stream)
+{
+    if (!C_batch || !H || !W_f || !b_f || (d_input > 0 && !X))
+        return fail(GSCAN_ERR_INVALID_ARGUMENT, "null pointer");
+    if (B < 1 || d_model < 1 || d_input < 0)
+        return fail(GSCAN_ERR_INVALID_ARGUMENT,
+                    "need B >= 1, d_model >= 1, d_input >= 0 (B=%lld d_model=%lld d_input=%lld)",
+                    (long long)B, (long long)d_model, (long long)d_input);
+    if (d_model % 4 != 0 || d_input % 4 != 0 || d_model > 16384 || d_input > (int64_t(1) << 24) ||
+        B > (int64_t(1) << 40) / (d_model * d_model))
+        return fail(GSCAN_ERR_UNSUPPORTED_SHAPE,
+                    "unsupported shape B=%lld d_model=%lld d_input=%lld (need d_model and d_input "
+                    "multiples of 4, d_model <= 16384, B*d_model^2 <= 2^40)",
+                    (long long)B, (long long)d_model, (long long)d_input);
+    if (!aligned16(C_batch) || !aligned16(H) || (d_input > 0 && !aligned16(X)) ||
+        !aligned16(W_f) || (reinterpret_cast<uintptr_t>(b_f) & 3u) != 0)
+        return fail(GSCAN_ERR_MISALIGNED,
+                    "C_batch, H, X, W_f must be 16-byte aligned and b_f 4-byte aligned");
+    // C_batch is updated in place and must not overlap any input
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(C_batch);
+    const uintptr_t c1 = c0 + (uintptr_t)(B * d_model * d_model) * sizeof(float);
+    auto overlaps = [&](const void *p, int64_t n) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(p);
+        return p && n > 0 && a0 < c1 && c0 < a0 + (uintptr_t)n * sizeof(float);
+    };
+    if (overlaps(H, B * d_model) || overlaps(X, B * d_input) ||
+        overlaps(W_f, d_model * (d_model + d_input)) || overlaps(b_f, d_model))
+        return fail(GSCAN_ERR_INVALID_ARGUMENT, "C_batch overlaps an input");
+    clear_stale_error();
+    hipError_t e = gscan::launch_cifg(C_batch, H, d_input > 0 ? X : H, W_f, b_f, B, d_model,
+                                      d_input, stream);
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "CIFG update launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return GSCAN_OK;
+}
+
 const char *gscan_status_string(int status)
 {
     switch (status) {

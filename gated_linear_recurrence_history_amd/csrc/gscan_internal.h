@@ -79,6 +79,10 @@ size_t colsum_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t launch_colsum(const float *grad, int64_t rows, int64_t cols, float *out,
                          void *workspace, hipStream_t stream);
 
+// CIFG matrix-memory update, independent mode, in place on C [B][d][d].
+hipError_t launch_cifg(float *C, const float *H, const float *X, const float *W_f,
+                       const float *b_f, int64_t B, int64_t d, int64_t din, hipStream_t stream);
+
 // Phase 2: fixed-order sum of the partials into dW_A, dW_B, dW_C.
 hipError_t launch_backward_reduce(const Plan &p, const float *partials, float *dW_A,
                                   float *dW_B, float *dW_C, hipStream_t stream);

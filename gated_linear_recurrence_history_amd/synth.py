@@ -97,3 +97,18 @@ def make_inputs(w: wl.Workload, seed: int | None = None, B: int | None = None,
     if with_grad:
         out["d_context"] = normal_f32(seed, wl.TID_D_CONTEXT, (B, w.D))
     return out
+
+
+def make_cifg_inputs(w: "wl.CifgWorkload", seed: int | None = None) -> dict:
+    """Host arrays for the CIFG update: C [B, d, d] ~ N(0, 1/d) (a memory of
+    modest norm), H [B, d] and X [B, d_input] ~ N(0, 1), W_f [d, d + d_input]
+    ~ N(0, 1/(d + d_input)), b_f [d] ~ N(0, 1); all float32."""
+    seed = w.seed if seed is None else seed
+    d, di = w.d_model, w.d_input
+    return {
+        "C": normal_f32(seed, wl.TID_CIFG_C, (w.B, d, d), 1.0 / np.sqrt(d)),
+        "H": normal_f32(seed, wl.TID_CIFG_H, (w.B, d)),
+        "X": normal_f32(seed, wl.TID_CIFG_X, (w.B, di)),
+        "W_f": normal_f32(seed, wl.TID_CIFG_W, (d, d + di), 1.0 / np.sqrt(d + di)),
+        "b_f": normal_f32(seed, wl.TID_CIFG_B, (d,)),
+    }

@@ -91,6 +91,40 @@ BY_NAME = {w.name: w for w in WORKLOADS}
 HEADLINE = BY_NAME["prod_fp32"]
 
 
+# ---- CIFG matrix-memory update (BURT-IMMA CUDA Kernel API Reference,
+# batched_cifg_update, independent mode).  The page quotes batch 32 with
+# d_model 512; the input width is not stated, so d_input = d_model is taken.
+TID_CIFG_C = 10
+TID_CIFG_H = 11
+TID_CIFG_X = 12
+TID_CIFG_W = 13
+TID_CIFG_B = 14
+
+CIFG_SEED = 20270
+
+
+@dataclasses.dataclass(frozen=True)
+class CifgWorkload:
+    name: str
+    B: int
+    d_model: int
+    d_input: int
+    seed: int = CIFG_SEED
+
+    def bytes(self) -> int:
+        """Algorithmic traffic: C read and written once, plus H, X, W_f, b_f read."""
+        d, di = self.d_model, self.d_input
+        return (2 * self.B * d * d + self.B * (d + di) + d * (d + di) + d) * 4
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "d_model": self.d_model,
+                "d_input": self.d_input}
+
+
+CIFG_PAGE = CifgWorkload("cifg_page", 32, 512, 512)
+CIFG_TOL = 1e-5  # fp32 throughout; see tests/test_gpu_cifg.py
+
+
 def tolerance(w: Workload) -> float:
     """Parity tolerance: context max |err| <= tol*(1+|ref|), dW rel-L2 <= tol."""
     return 2e-2 if w.in_dtype == "bf16" else 1e-4

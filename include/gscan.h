@@ -207,6 +207,29 @@ size_t gscan_backward_full_workspace_bytes(int64_t B, int64_t K, int64_t SH2, in
 int gscan_bias_grad_reduce(const float *grad, int64_t rows, int64_t cols, float *out,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * CIFG matrix-memory update, independent mode (BURT-IMMA CUDA Kernel API
+ * Reference, section 2.3 batched_cifg_update with shared_memory_mode =
+ * false: section 2.2 cifg_update, steps 1-4, for every sample):
+ *   concat = [h_b ; x_b]                                (d_model + d_input)
+ *   f      = sigmoid(W_f @ concat + b_f)                (d_model)
+ *   C_b[i][j] <- f[i] * C_b[i][j] + (1 - f[i]) * h_b[i] * h_b[j]
+ * in place on C_batch [B][d_model][d_model] (fp32 row-major); H [B][d_model],
+ * X [B][d_input] (may be NULL when d_input == 0), W_f [d_model][d_model +
+ * d_input] (its first d_model columns act on h), b_f [d_model]; all fp32
+ * device memory, C_batch, H, X, W_f 16-byte aligned, b_f 4-byte aligned.
+ * C_batch must not overlap any input.  Step 5 of cifg_update (the optional
+ * spectral clip by a power iteration) and the shared-memory mode are not
+ * provided.  Arithmetic is fp32; the gate's dot product is summed in a
+ * fixed order (bitwise reproducible).  Errors: INVALID_ARGUMENT (null
+ * pointer, B < 1, d_model < 1, d_input < 0, overlap), UNSUPPORTED_SHAPE
+ * (d_model or d_input not a multiple of 4, d_model > 16384,
+ * B * d_model^2 > 2^40), MISALIGNED, HIP_ERROR; nothing is launched on error.
+ */
+int gscan_batched_cifg_update(float *C_batch, const float *H, const float *X,
+                              const float *W_f, const float *b_f, int64_t B, int64_t d_model,
+                              int64_t d_input, hipStream_t stream);
+
 /* Workspace bytes of gscan_bias_grad_reduce (0 for invalid sizes). */
 size_t gscan_bias_grad_reduce_workspace_bytes(int64_t rows, int64_t cols);
 

@@ -191,3 +191,28 @@ def _enrich(lib, B=64, K=8, SH2=256, D=16, ctx=None, he=FAKE, ld=256, off=0, dty
 def test_forward_enrich_validation(lib, kw, code):
     assert _enrich(lib, **kw) == code
     assert lib.gscan_last_error() != b""
+
+
+def _cifg(lib, C=FAKE, H=FAKE + 0x100000, X=FAKE + 0x200000, W=FAKE + 0x300000,
+          b=FAKE + 0x400000, B=2, d=8, din=4):
+    return lib.gscan_batched_cifg_update(C, H, X, W, b, B, d, din, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(C=None), INVALID), (dict(H=None), INVALID), (dict(X=None), INVALID),
+    (dict(W=None), INVALID), (dict(b=None), INVALID), (dict(B=0), INVALID), (dict(d=0), INVALID),
+    (dict(din=-4), INVALID), (dict(d=6), UNSUPPORTED), (dict(din=3), UNSUPPORTED),
+    (dict(d=16388), UNSUPPORTED), (dict(C=FAKE + 8), MISALIGNED), (dict(X=FAKE + 0x200004), MISALIGNED),
+    (dict(b=FAKE + 0x400002), MISALIGNED),
+    # C_batch [2, 8, 8] spans 512 bytes: H placed inside it overlaps
+    (dict(H=FAKE + 256), INVALID),
+])
+def test_cifg_validation(lib, kw, code):
+    assert _cifg(lib, **kw) == code
+    assert lib.gscan_last_error() != b""
+
+
+def test_cifg_x_may_be_null_without_input(lib):
+    # d_input == 0 accepts X = NULL (validation passes up to the launch, which
+    # is not reached here because C is misaligned on purpose)
+    assert _cifg(lib, X=None, din=0, C=FAKE + 4) == MISALIGNED

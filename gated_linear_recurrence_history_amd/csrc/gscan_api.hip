@@ -92,6 +92,12 @@ FullLayout full_layout(const gscan::Plan &p)
 {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     FullLayout f;
+    if (p.bwd_split) {  // the split backward's workspace already holds both
+        f.dab = p.split_dab;
+        f.dc = p.split_dc;
+        f.bytes = p.ws_bytes;
+        return f;
+    }
     f.dab = up(p.ws_bytes);
     f.dc = up(f.dab + (size_t)(p.B * p.K) * (size_t)(2 * p.D) * sizeof(float));
     f.bytes = f.dc + (size_t)p.B * (size_t)p.D * sizeof(float);
@@ -312,7 +318,7 @@ int gscan_backward_full_ex(const void *h_history, const void *h_s2, const float 
     hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
                                                    d_context, part, dab, dc, stream);
     if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
-    if (e == hipSuccess && !plan.bwd_rows_kernel)
+    if (e == hipSuccess && !plan.adjoints_final())
         e = gscan::launch_adjoint(plan, dab, dc, d_context, a_shift, stream);
     if (e == hipSuccess)
         e = gscan::launch_dinput(dab, W_A, W_B, D, 2 * D, SH2, B * K, d_h_history, stream);

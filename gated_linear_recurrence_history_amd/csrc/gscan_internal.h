@@ -35,7 +35,16 @@ struct Plan {
     int64_t bwd_grid = 0;
     int64_t red_grid = 0;
     bool bwd_rows_kernel = false;  // backward via the K-divides-16 kernel
-    size_t ws_bytes = 0;    // weight-gradient partials: bwd_rows x 3 x SH2 x D floats
+    // split backward (scan pass, then contraction over row slabs): the
+    // workspace holds the slab partials, dL/dA | dL/dB per row at split_dab
+    // and dL/dC per sample at split_dc (byte offsets)
+    bool bwd_split = false;
+    int64_t split_slabs = 0;
+    int64_t ps_grid = 0;
+    size_t split_dab = 0, split_dc = 0;
+    size_t ws_bytes = 0;    // the backward's workspace (partials, and the split pass's adjoints)
+    // phase 1 leaves the final dL/dA | dL/dB and dL/dC (not projections)
+    bool adjoints_final() const { return bwd_rows_kernel || bwd_split; }
 };
 
 // Where the forward writes context[b][s]: the context output (null: not

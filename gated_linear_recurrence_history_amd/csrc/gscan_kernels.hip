@@ -44,6 +44,7 @@
 // The backward runs the same construction on the reverse adjoint
 //   mu_{r-1} = g_r * mu_r (t_r > 0),   mu_{r-1} = lambda_K(previous sample) (t_r = 0).
 #include <cstdint>
+#include <type_traits>
 
 #include "gscan_internal.h"
 
@@ -1899,6 +1900,424 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     }
 }
 
+// ======================== split backward: projection + scans, then contraction
+// For wide rows (SH2 = 512, where the per-block kernel's LDS budget ends) and
+// long scans the backward is split in two passes:
+//   gscan_bwd_scan_kernel      projection replay, forward and reverse scans:
+//                              dL/dA | dL/dBv per row ([B*K][2D] fp32) and
+//                              dL/dC per sample ([B][D]) into the workspace
+//   gscan_bwd_contract_kernel  the weight-gradient contractions as MFMA
+//                              tiles over row slabs: h_history^T @ [dA | dB]
+//                              and h_s2^T @ dC, one partial per slab
+// followed by the fixed-order reduction of the partials.
+//
+// Scan pass.  A tile is 256 rows holding whole samples (K divides 256 and
+// is a multiple of 32), so every wavefront's 32 rows (two MFMA row blocks)
+// belong to one sample.  A workgroup of 8 wavefronts owns 32 states (two
+// 16-state slices), keeps their A|B weights as one split image in LDS and
+// walks tiles persistently; the state groups of a tile run on one XCD at
+// the same time, so the tile's rows come from HBM once and from L2 for the
+// other groups.  Per tile: the C values of its samples (fp32 dot products
+// against W_C columns held in registers), the A|B projection of each row
+// block unit by unit (row data four units ahead, running on into the next
+// tile), the gates and their complements, the lane-level scans, one
+// exchange of per-wavefront maps through LDS, then the walks that give
+// x_t, lambda_{t+1} and the adjoints of every row.
+constexpr int kPsWaves = 8;
+constexpr int kPsThreads = kWave * kPsWaves;
+constexpr int kPsRows = 256;       // rows per tile
+constexpr int kPsStates = 32;      // states per workgroup
+constexpr int kPsDepth = 4;        // units of row data in flight
+
+template <typename TIn, int NQ> struct PsRing;
+
+template <int NQ> struct PsRing<float, NQ> {
+    f4 v[kPsDepth][2][2];  // [slot][row block][half]
+    __device__ __forceinline__ void load(const float *const *row, int kg, int q, int slot)
+    {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            v[slot][rb][0] = *reinterpret_cast<const f4 *>(row[rb] + 32 * q + 8 * kg);
+            v[slot][rb][1] = *reinterpret_cast<const f4 *>(row[rb] + 32 * q + 8 * kg + 4);
+        }
+    }
+    __device__ __forceinline__ Split op(int slot, int rb) const
+    {
+        float x[8] = {v[slot][rb][0][0], v[slot][rb][0][1], v[slot][rb][0][2], v[slot][rb][0][3],
+                      v[slot][rb][1][0], v[slot][rb][1][1], v[slot][rb][1][2], v[slot][rb][1][3]};
+        return split8(x);
+    }
+};
+
+template <int NQ> struct PsRing<uint16_t, NQ> {
+    u4 v[kPsDepth][2];
+    __device__ __forceinline__ void load(const uint16_t *const *row, int kg, int q, int slot)
+    {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            v[slot][rb] = *reinterpret_cast<const u4 *>(row[rb] + 32 * q + 8 * kg);
+    }
+    __device__ __forceinline__ Split op(int slot, int rb) const
+    {
+        Split s;
+        s.hi = v[slot][rb];
+        s.lo = zero_u4();
+        return s;
+    }
+};
+
+// workgroup -> (state group, first tile): the nsg state groups of a tile sit
+// on one XCD (blockIdx % 8) next to each other
+__device__ __forceinline__ void ps_decode(int nsg, int &sg, int64_t &tile0, int64_t &tstride)
+{
+    const int id = blockIdx.x;
+    const int xcd = id % kXcds, r = id / kXcds;
+    sg = r % nsg;
+    tile0 = (int64_t)(r / nsg) * kXcds + xcd;
+    tstride = gridDim.x / nsg;
+}
+
+template <typename TIn, int NQ, int KT>
+__global__ void __launch_bounds__(kPsThreads, 1)
+gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
+                      const float *__restrict__ WA, const float *__restrict__ WB,
+                      const float *__restrict__ WC, int64_t ntiles, int D, float a_shift,
+                      const float *__restrict__ dctx, float *__restrict__ dab,
+                      float *__restrict__ dcv)
+{
+    constexpr int SH2 = NQ * 32;
+    constexpr int S = 2;
+    constexpr bool LO = PBlk<TIn, NQ>::kLo;
+    constexpr int NS = kPsRows / KT;   // samples per tile
+    constexpr int WPS = KT / 32;       // wavefronts per sample
+    constexpr int KP = SH2 / 16;       // W_C rows per thread part (C values)
+    static_assert(KT % 32 == 0 && kPsRows % KT == 0, "whole samples per tile and wavefront");
+    static_assert(NQ >= kPsDepth, "ring deeper than a row");
+    __shared__ u4 img[S * NQ * 4 * kWave];
+    __shared__ float credp[16][NS][kPsStates];     // C partials by k part
+    __shared__ float cl[2][NS][kPsStates];         // C, by tile parity
+    __shared__ float dcl[2][NS][kPsStates];        // d_context, by tile parity
+    __shared__ float fmap[2][kPsWaves][S][2][16];  // wavefront maps (M, C), by tile parity
+    __shared__ float gprod[2][kPsWaves][S][16];    // wavefront gate products, by tile parity
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = wave_id();
+    const int kg = lane >> 4, ln = lane & 15;
+    const int nsg = D / kPsStates;
+    int sg;
+    int64_t tile, tstride;
+    ps_decode(nsg, sg, tile, tstride);
+    const int s0 = sg * kPsStates;
+
+    // this wavefront's rows of a tile: 32 * wave + 16 * rb + (lane % 16)
+    auto rows_of = [&](int64_t t, const TIn **row) {
+        const int64_t tt = t < ntiles ? t : ntiles - 1;  // past the end: a valid tile, unused
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            row[rb] = hh + (tt * kPsRows + 32 * wave + 16 * rb + ln) * (int64_t)SH2;
+    };
+    PsRing<TIn, NQ> ring;
+    const TIn *rcur[2];
+    rows_of(tile, rcur);
+#pragma unroll
+    for (int q = 0; q < kPsDepth; ++q) ring.load(rcur, kg, q, q);
+
+    // W_C rows cp*KP .. +KP-1 of state s0 + cs, for the C values
+    const int cs = tid % kPsStates, cp = tid / kPsStates;
+    float wc[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) wc[k] = WC[(int64_t)(cp * KP + k) * D + s0 + cs];
+    stage_image<NQ, S, 2>(img, WA, WB, D, s0);
+    __syncthreads();
+
+    for (int par = 0; tile < ntiles; tile += tstride, par ^= 1) {
+        const int64_t bt = tile * NS;  // first sample of the tile
+        // ---- C partials of the tile's samples (plain fp32 dot products)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const TIn *hp = hs2 + (bt + j) * SH2 + cp * KP;
+            float acc = 0.f;
+#pragma unroll
+            for (int k = 0; k < KP; ++k) {
+                float hv;
+                if constexpr (LO) hv = hp[k];
+                else hv = __uint_as_float((uint32_t)hp[k] << 16);
+                acc = fmaf(hv, wc[k], acc);
+            }
+            credp[cp][j][cs] = acc;
+        }
+
+        // ---- A|Bv projection of both row blocks, both slices
+        const TIn *rnxt[2];
+        rows_of(tile + tstride, rnxt);
+        f4 aA[S][2], aB[S][2];
+#pragma unroll
+        for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                aA[sl][rb] = zero4();
+                aB[sl][rb] = zero4();
+            }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int slot = q % kPsDepth;
+            const Split h0 = ring.op(slot, 0), h1 = ring.op(slot, 1);
+            // the slot takes unit q + depth (of this tile, or of the next)
+            if (q + kPsDepth < NQ) ring.load(rcur, kg, q + kPsDepth, slot);
+            else ring.load(rnxt, kg, q + kPsDepth - NQ, slot);
+#pragma unroll
+            for (int sl = 0; sl < S; ++sl) {
+                const Split wa = img_op(img, (sl * NQ + q) * 2, lane);
+                const Split wb = img_op(img, (sl * NQ + q) * 2 + 1, lane);
+                aA[sl][0] = mfma3<LO>(h0, wa, aA[sl][0]);
+                aA[sl][1] = mfma3<LO>(h1, wa, aA[sl][1]);
+                aB[sl][0] = mfma3<LO>(h0, wb, aB[sl][0]);
+                aB[sl][1] = mfma3<LO>(h1, wb, aB[sl][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        rcur[0] = rnxt[0];
+        rcur[1] = rnxt[1];
+
+        // ---- gates and the lane-level scans.  Row 4*kg + j of block rb.
+        float gt[S][2][4], gc[S][2][4];
+        Aff excl[S][2], tot[S][2];
+        float gsuf[S][2], gall[S][2];
+#pragma unroll
+        for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                Aff F = aff_id();
+                float G = 1.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const Gate g = gate_of(aA[sl][rb][j] + a_shift);
+                    gt[sl][rb][j] = g.g;
+                    gc[sl][rb][j] = g.gc;
+                    Aff m = {g.g, aB[sl][rb][j], 0};
+                    F = compose(m, F);
+                    G *= g.g;
+                }
+                scan_up(F, lane, excl[sl][rb], tot[sl][rb]);
+                // gate products of the later lane groups of the block, and of all four
+                const RowVals pg = pair_rows(G);
+                const bool odd = kg & 1;
+                const float pp = pg.lo * pg.hi;
+                const RowVals hp = half_rows(pp);
+                gsuf[sl][rb] = (odd ? 1.f : pg.hi) * (kg < 2 ? hp.hi : 1.f);
+                gall[sl][rb] = hp.lo * hp.hi;
+            }
+        // the wavefront's own map and gate product
+        if (kg == 0) {
+#pragma unroll
+            for (int sl = 0; sl < S; ++sl) {
+                const Aff w = compose(tot[sl][1], tot[sl][0]);
+                fmap[par][wave][sl][0][ln] = w.m;
+                fmap[par][wave][sl][1][ln] = w.c;
+                gprod[par][wave][sl][ln] = gall[sl][0] * gall[sl][1];
+            }
+        }
+        __syncthreads();
+        // ---- C and d_context of the tile's samples
+        if (tid < NS * kPsStates) {
+            const int j = tid / kPsStates, s = tid % kPsStates;
+            float c = 0.f;
+#pragma unroll
+            for (int p = 0; p < 16; ++p) c += credp[p][j][s];
+            cl[par][j][s] = c;
+            dcl[par][j][s] = dctx[(bt + j) * D + s0 + s];
+        }
+        __syncthreads();
+
+        // ---- cross-wavefront folds, walks, adjoints
+        const int sj = wave / WPS;            // sample of this wavefront in the tile
+        const int w0 = sj * WPS;              // its first wavefront
+        const int64_t row0 = tile * kPsRows + 32 * wave;
+#pragma unroll
+        for (int sl = 0; sl < S; ++sl) {
+            const int st = 16 * sl + ln;      // state within the group
+            // state entering the wavefront: earlier wavefronts of the sample
+            float xin = 0.f;
+            for (int w2 = w0; w2 < wave; ++w2)
+                xin = fmap[par][w2][sl][0][ln] * xin + fmap[par][w2][sl][1][ln];
+            // adjoint entering the wavefront's last row: lambda_K times the
+            // gates of the sample's later wavefronts
+            float lin = dcl[par][sj][st] * cl[par][sj][st];
+            for (int w2 = wave + 1; w2 < w0 + WPS; ++w2) lin *= gprod[par][w2][sl][ln];
+            float xbef[2][4];
+            float x = apply(excl[sl][0], xin);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                if (rb == 1) x = apply(excl[sl][1], apply(tot[sl][0], xin));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xbef[rb][j] = x;
+                    x = gt[sl][rb][j] * x + aB[sl][rb][j];
+                }
+            }
+            // the sample's last row (block 1, lane group 3, j = 3): dL/dC
+            if (wave == w0 + WPS - 1 && kg == 3)
+                dcv[(bt + sj) * D + s0 + st] = dcl[par][sj][st] * x;
+#pragma unroll
+            for (int rb = 1; rb >= 0; --rb) {
+                float mu = lin * gsuf[sl][rb] * (rb == 0 ? gall[sl][1] : 1.f);
+                float *o = dab + (row0 + 16 * rb + 4 * kg) * (int64_t)(2 * D) + s0 + st;
+#pragma unroll
+                for (int j = 3; j >= 0; --j) {
+                    o[j * 2 * D + D] = mu;                                           // dL/dBv
+                    o[j * 2 * D] = mu * xbef[rb][j] * (gt[sl][rb][j] * gc[sl][rb][j]);  // dL/dA
+                    mu = gt[sl][rb][j] * mu;
+                }
+            }
+        }
+    }
+}
+
+// ---- contraction: part[slab][which0 + o / D][i][o % D] = sum over the
+// slab's rows r of X[r][i] * Y[r][o], for i in [m0, m0 + MT), o in
+// [n0, n0 + NT).  32 rows per step: both tiles are split into bf16 high /
+// low planes in LDS (row-major, rows padded by 8 columns) and read back
+// transposed with ds_read_b64_tr_b16, so lane l gets column l % 16 of rows
+// 4(l/16) .. +3 and 16 + 4(l/16) .. +3: the MFMA k index 8(l/16) + e for
+// both operands.  Double-buffered: one barrier per step; the next step's
+// rows are requested before the current step is contracted.
+constexpr int kCtThreads = 512;
+constexpr int kCtRows = 32;
+
+template <typename TX, int MT, int NT>
+__global__ void __launch_bounds__(kCtThreads, 1)
+gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__restrict__ Y, int ldy,
+                          int64_t rows, int64_t rows_per_slab, int D, int which0,
+                          int SH2, float *__restrict__ part)
+{
+    constexpr bool LO = !std::is_same<TX, uint16_t>::value;
+    constexpr int kPl = LO ? 2 : 1;               // planes of X
+    constexpr int PX = MT + 8, PY = NT + 8;       // LDS row pitches (bf16)
+    constexpr int WN = NT / 64, WM = 8 / WN;      // wavefront grid
+    constexpr int MTW = MT / 16 / WM;             // m tiles per wavefront
+    constexpr int XV = kCtRows * MT / (LO ? 4 : 8) / kCtThreads;  // X pieces per thread
+    constexpr int YV = kCtRows * NT / 4 / kCtThreads;             // Y pieces per thread
+    static_assert(XV >= 1 && YV >= 1, "pieces per thread");
+    __shared__ uint16_t xs[2][kPl][kCtRows][PX];
+    __shared__ uint16_t ys[2][2][kCtRows][PY];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = wave_id();
+    const int kg = lane >> 4, ln = lane & 15;
+    const int wm = wave % WM, wn = wave / WM;
+    const int64_t slab = blockIdx.x;
+    const int m0 = blockIdx.y * MT, n0 = blockIdx.z * NT;
+    const int64_t r_begin = slab * rows_per_slab;
+    const int64_t r_end = r_begin + rows_per_slab < rows ? r_begin + rows_per_slab : rows;
+
+    typedef typename std::conditional<LO, f4, u4>::type xraw_t;
+    xraw_t xv[XV];
+    f4 yv[YV];
+    constexpr int XCOLS = LO ? MT / 4 : MT / 8;   // pieces per X row
+    auto load = [&](int64_t rb) {
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int e = tid + kCtThreads * u;
+            const int r = e / XCOLS, c = e % XCOLS;
+            const int64_t gr = rb + r;
+            if (gr < r_end) {
+                if constexpr (LO)
+                    xv[u] = *reinterpret_cast<const f4 *>(X + gr * ldx + m0 + 4 * c);
+                else
+                    xv[u] = *reinterpret_cast<const u4 *>(X + gr * ldx + m0 + 8 * c);
+            } else {
+                if constexpr (LO) xv[u] = zero4();
+                else xv[u] = zero_u4();
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < YV; ++u) {
+            const int e = tid + kCtThreads * u;
+            const int r = e / (NT / 4), c = e % (NT / 4);
+            const int64_t gr = rb + r;
+            yv[u] = gr < r_end ? *reinterpret_cast<const f4 *>(Y + gr * ldy + n0 + 4 * c) : zero4();
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int e = tid + kCtThreads * u;
+            const int r = e / XCOLS, c = e % XCOLS;
+            if constexpr (LO) {
+                const uint32_t h01 = pack_bf16(xv[u][0], xv[u][1]), h23 = pack_bf16(xv[u][2], xv[u][3]);
+                const uint32_t l01 = pack_bf16(xv[u][0] - bf_lo(h01), xv[u][1] - bf_hi(h01));
+                const uint32_t l23 = pack_bf16(xv[u][2] - bf_lo(h23), xv[u][3] - bf_hi(h23));
+                *reinterpret_cast<uint2 *>(&xs[buf][0][r][4 * c]) = uint2{h01, h23};
+                *reinterpret_cast<uint2 *>(&xs[buf][kPl - 1][r][4 * c]) = uint2{l01, l23};
+            } else {
+                *reinterpret_cast<u4 *>(&xs[buf][0][r][8 * c]) = xv[u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < YV; ++u) {
+            const int e = tid + kCtThreads * u;
+            const int r = e / (NT / 4), c = e % (NT / 4);
+            const uint32_t h01 = pack_bf16(yv[u][0], yv[u][1]), h23 = pack_bf16(yv[u][2], yv[u][3]);
+            const uint32_t l01 = pack_bf16(yv[u][0] - bf_lo(h01), yv[u][1] - bf_hi(h01));
+            const uint32_t l23 = pack_bf16(yv[u][2] - bf_lo(h23), yv[u][3] - bf_hi(h23));
+            *reinterpret_cast<uint2 *>(&ys[buf][0][r][4 * c]) = uint2{h01, h23};
+            *reinterpret_cast<uint2 *>(&ys[buf][1][r][4 * c]) = uint2{l01, l23};
+        }
+    };
+    // transposed operand: column c + ln of rows 4kg..+3 and 16 + 4kg..+3
+    auto operand = [&](const uint16_t *tile, int pitch, int c) {
+        const uint16_t *p = tile + (4 * kg + (ln >> 2)) * pitch + c + 4 * (ln & 3);
+        const uint2 a = read_tr(p), b = read_tr(p + 16 * pitch);
+        return u4{a.x, a.y, b.x, b.y};
+    };
+
+    f4 acc[MTW][4];
+#pragma unroll
+    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+
+    if (r_begin < r_end) {
+        load(r_begin);
+        int buf = 0;
+        for (int64_t rb = r_begin; rb < r_end; rb += kCtRows, buf ^= 1) {
+            store(buf);
+            __syncthreads();  // this buffer written; the other one's readers are done
+            if (rb + kCtRows < r_end) load(rb + kCtRows);
+            Split bo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 64 * wn + 16 * j;
+                bo[j].hi = operand(&ys[buf][0][0][0], PY, c);
+                bo[j].lo = operand(&ys[buf][1][0][0], PY, c);
+            }
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) {
+                const int c = 16 * (MTW * wm + i);
+                Split ao;
+                ao.hi = operand(&xs[buf][0][0][0], PX, c);
+                ao.lo = LO ? operand(&xs[buf][kPl - 1][0][0], PX, c) : zero_u4();
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma3<LO>(ao, bo[j], acc[i][j]);
+            }
+        }
+    }
+    // partial of this slab: lane l holds i = m-tile row 4(l/16) + e, o = l % 16
+    float *P = part + slab * 3 * (int64_t)SH2 * D;
+#pragma unroll
+    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int o = n0 + 64 * wn + 16 * j + ln;
+            const int which = which0 + o / D, s = o % D;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ii = m0 + 16 * (MTW * wm + i) + 4 * kg + e;
+                P[((int64_t)which * SH2 + ii) * D + s] = acc[i][j][e];
+            }
+        }
+}
+
 // ================================================= phase 2: partial reduction
 // Workgroup = 32 consecutive gradient entries; thread (seg, quad) sums rows
 // r = seg, seg+32, ... of four consecutive entries, eight rows in flight at
@@ -2097,11 +2516,61 @@ hipError_t fwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
     return hipGetLastError();
 }
 
+// the split backward: scan pass, then the two contractions into slab partials
+template <typename TIn, int NQ>
+hipError_t split_launch(const Plan &p, const void *hh, const void *hs2, const float *WA,
+                        const float *WB, const float *WC, float a_shift, const float *dctx,
+                        float *part, float *dab, float *dc, hipStream_t st)
+{
+    char *ws = reinterpret_cast<char *>(part);
+    float *ab = dab ? dab : reinterpret_cast<float *>(ws + p.split_dab);
+    float *cv = dc ? dc : reinterpret_cast<float *>(ws + p.split_dc);
+    const int64_t ntiles = p.B * p.K / kPsRows;
+    auto scan = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.ps_grid), dim3(kPsThreads), 0, st,
+                           static_cast<const TIn *>(hh), static_cast<const TIn *>(hs2), WA, WB, WC,
+                           ntiles, (int)p.D, a_shift, dctx, ab, cv);
+        return hipGetLastError();
+    };
+    hipError_t e;
+    if constexpr (NQ == 8 || NQ == 16) {
+        if (p.K == 64) e = scan(gscan_bwd_scan_kernel<TIn, NQ, 64>);
+        else if (p.K == 256) e = scan(gscan_bwd_scan_kernel<TIn, NQ, 256>);
+        else return hipErrorInvalidValue;
+    } else {
+        return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    const int64_t rows = p.B * p.K;
+    const int64_t rps = (rows + p.split_slabs - 1) / p.split_slabs;
+    const int64_t rpsc = (p.B + p.split_slabs - 1) / p.split_slabs;
+    const int sh2 = (int)p.SH2, d = (int)p.D;
+    // h_history^T @ [dA | dB]: 2D outputs in tiles of 128
+    hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128>),
+                       dim3((unsigned)p.split_slabs, (unsigned)(p.SH2 / 256), (unsigned)(2 * p.D / 128)),
+                       dim3(kCtThreads), 0, st, static_cast<const TIn *>(hh), sh2,
+                       (const float *)ab, 2 * d, rows, rps, d, 0, sh2, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // h_s2^T @ dC: D outputs in tiles of 128, or 64
+    if (p.D % 128 == 0)
+        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128>),
+                           dim3((unsigned)p.split_slabs, (unsigned)(p.SH2 / 256), (unsigned)(p.D / 128)),
+                           dim3(kCtThreads), 0, st, static_cast<const TIn *>(hs2), sh2,
+                           (const float *)cv, d, p.B, rpsc, d, 2, sh2, part);
+    else
+        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 64>),
+                           dim3((unsigned)p.split_slabs, (unsigned)(p.SH2 / 256), (unsigned)(p.D / 64)),
+                           dim3(kCtThreads), 0, st, static_cast<const TIn *>(hs2), sh2,
+                           (const float *)cv, d, p.B, rpsc, d, 2, sh2, part);
+    return hipGetLastError();
+}
+
 template <typename TIn, int NQ>
 hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const float *WA,
                       const float *WB, const float *WC, float a_shift, const float *dctx,
                       float *part, float *dab, float *dc, hipStream_t st)
 {
+    if (p.bwd_split) return split_launch<TIn, NQ>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, st);
     const bool aligned = 16 % p.K == 0;
     if constexpr (NQ <= 8) {
         if (p.bwd_rows_kernel) {
@@ -2217,6 +2686,29 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
     const int64_t wsz = SH2 * D;
     q.red_grid = 3 * wsz / kRedCols;
     q.ws_bytes = (size_t)(q.bwd_rows * 3 * wsz * 4);
+    // split backward for the widest rows (SH2 = 512, beyond the per-block
+    // kernel's LDS budget) when whole samples fill 256-row tiles (K = 64 or
+    // 256 compiled) and the states come in groups of 64
+    const int64_t ns = K > 0 && kPsRows % K == 0 ? kPsRows / K : 0;
+    if (SH2 == 512 && D % 64 == 0 && (K == 64 || K == 256) && ns > 0 && B % ns == 0) {
+        q.bwd_split = true;
+        q.bwd_rows_kernel = false;
+        const int64_t ntiles = B * K / kPsRows;
+        const int64_t nsg = D / kPsStates;
+        const int64_t cap = 256 / (8 * nsg) * (8 * nsg);
+        const int64_t want = (ntiles + 7) / 8 * 8 * nsg;
+        q.ps_grid = want < cap ? want : cap;
+        const int64_t tiles_per_slab = (SH2 / 256) * (2 * D / 128);
+        int64_t slabs = 256 / tiles_per_slab;
+        if (slabs < 1) slabs = 1;
+        q.split_slabs = slabs;
+        auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+        const size_t part = (size_t)(slabs * 3 * wsz * 4);
+        q.split_dab = up(part);
+        q.split_dc = up(q.split_dab + (size_t)(B * K) * (size_t)(2 * D) * sizeof(float));
+        q.ws_bytes = q.split_dc + (size_t)(B * D) * sizeof(float);
+        q.bwd_rows = slabs;  // the reduction sums one partial per slab
+    }
     if (q.fwd_grid > 0x7fffffff || q.bwd_grid > 0x7fffffff) return false;
     *p = q;
     return true;
@@ -2286,7 +2778,8 @@ hipError_t launch_dinput(const float *in, const float *W1, const float *W2, int6
 hipError_t launch_backward_reduce(const Plan &p, const float *part, float *dWA, float *dWB,
                                   float *dWC, hipStream_t st)
 {
-    // the per-block kernel writes its partials in the quad layout
+    // the per-block kernel writes its partials in the quad layout; the
+    // general kernel and the split contraction in [which][i][s]
     hipLaunchKernelGGL(gscan_reduce_kernel, dim3((unsigned)p.red_grid), dim3(kThreads), 0, st,
                        part, p.bwd_rows, p.SH2 * p.D, (int)p.D, p.bwd_rows_kernel ? 1 : 0, dWA,
                        dWB, dWC);

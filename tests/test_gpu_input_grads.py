@@ -36,6 +36,8 @@ SHAPES = [
     (70, 2, 256, 16, "f32", 0.0),
     (21, 32, 128, 32, "f32", -1.0),   # samples of 2 blocks (per-block kernel)
     (9, 64, 64, 16, "bf16", 0.5),     # samples of 4 blocks
+    (8, 64, 512, 64, "f32", 1.0),     # split backward: adjoints straight from the scan pass
+    (2, 256, 512, 128, "bf16", -0.5),
 ]
 
 

@@ -75,6 +75,16 @@ SMALL = [
     (45, 8, 64, 16, "f32", 0.5),
     (29, 8, 192, 48, "bf16", 2.0),
     (19, 64, 128, 16, "f32", 0.0),
+    # SH2 = 512 with K = 64 or 256 and whole samples per 256-row tile: the
+    # split backward (scan pass, contraction over row slabs): state groups
+    # of 64, 128 and 192, bf16 rows, a_shift, several tiles per workgroup,
+    # and a batch that is not a multiple of four (the general kernel again)
+    (12, 64, 512, 64, "f32", 2.0),
+    (8, 64, 512, 128, "bf16", 0.5),
+    (3, 256, 512, 64, "f32", -1.0),
+    (20, 64, 512, 192, "f32", 0.25),
+    (2000, 64, 512, 64, "f32", 1.0),
+    (13, 64, 512, 64, "f32", 0.0),
 ]
 
 

@@ -1929,6 +1929,13 @@ constexpr int kPsRows = 256;       // rows per tile
 constexpr int kPsStates = 32;      // states per workgroup
 constexpr int kPsDepth = 4;        // units of row data in flight
 
+// The row pointers pass through the tile loop's registers, where the
+// compiler no longer sees that they address global memory; the loads name
+// the address space so that they are global (not flat) loads, whose waits
+// do not also wait for LDS traffic.
+typedef const __attribute__((address_space(1))) f4 gf4;
+typedef const __attribute__((address_space(1))) u4 gu4;
+
 template <typename TIn, int NQ> struct PsRing;
 
 template <int NQ> struct PsRing<float, NQ> {
@@ -1937,8 +1944,8 @@ template <int NQ> struct PsRing<float, NQ> {
     {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            v[slot][rb][0] = *reinterpret_cast<const f4 *>(row[rb] + 32 * q + 8 * kg);
-            v[slot][rb][1] = *reinterpret_cast<const f4 *>(row[rb] + 32 * q + 8 * kg + 4);
+            v[slot][rb][0] = *(gf4 *)(row[rb] + 32 * q + 8 * kg);
+            v[slot][rb][1] = *(gf4 *)(row[rb] + 32 * q + 8 * kg + 4);
         }
     }
     __device__ __forceinline__ Split op(int slot, int rb) const
@@ -1955,7 +1962,7 @@ template <int NQ> struct PsRing<uint16_t, NQ> {
     {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
-            v[slot][rb] = *reinterpret_cast<const u4 *>(row[rb] + 32 * q + 8 * kg);
+            v[slot][rb] = *(gu4 *)(row[rb] + 32 * q + 8 * kg);
     }
     __device__ __forceinline__ Split op(int slot, int rb) const
     {
@@ -2022,11 +2029,10 @@ gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 #pragma unroll
     for (int q = 0; q < kPsDepth; ++q) ring.load(rcur, kg, q, q);
 
-    // W_C rows cp*KP .. +KP-1 of state s0 + cs, for the C values
+    // thread (cp, cs) forms the part of C over W_C rows cp*KP .. +KP-1 for
+    // state s0 + cs (the W_C values come from L2 each tile)
     const int cs = tid % kPsStates, cp = tid / kPsStates;
-    float wc[KP];
-#pragma unroll
-    for (int k = 0; k < KP; ++k) wc[k] = WC[(int64_t)(cp * KP + k) * D + s0 + cs];
+    const float *const wcp = WC + (int64_t)(cp * KP) * D + s0 + cs;
     stage_image<NQ, S, 2>(img, WA, WB, D, s0);
     __syncthreads();
 
@@ -2042,7 +2048,7 @@ gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                 float hv;
                 if constexpr (LO) hv = hp[k];
                 else hv = __uint_as_float((uint32_t)hp[k] << 16);
-                acc = fmaf(hv, wc[k], acc);
+                acc = fmaf(hv, wcp[(int64_t)k * D], acc);
             }
             credp[cp][j][cs] = acc;
         }
@@ -2164,7 +2170,7 @@ gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                 float *o = dab + (row0 + 16 * rb + 4 * kg) * (int64_t)(2 * D) + s0 + st;
 #pragma unroll
                 for (int j = 3; j >= 0; --j) {
-                    o[j * 2 * D + D] = mu;                                           // dL/dBv
+                    o[j * 2 * D + D] = mu;                                              // dL/dBv
                     o[j * 2 * D] = mu * xbef[rb][j] * (gt[sl][rb][j] * gc[sl][rb][j]);  // dL/dA
                     mu = gt[sl][rb][j] * mu;
                 }
@@ -2179,12 +2185,14 @@ gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 // low planes in LDS (row-major, rows padded by 8 columns) and read back
 // transposed with ds_read_b64_tr_b16, so lane l gets column l % 16 of rows
 // 4(l/16) .. +3 and 16 + 4(l/16) .. +3: the MFMA k index 8(l/16) + e for
-// both operands.  Double-buffered: one barrier per step; the next step's
-// rows are requested before the current step is contracted.
+// both operands.  The eight wavefronts form a WM x WN grid over the tile.
+// Two register sets hold the rows of the next two steps, so a step's loads
+// have two steps of compute to arrive; double-buffered LDS, one barrier per
+// step.
 constexpr int kCtThreads = 512;
 constexpr int kCtRows = 32;
 
-template <typename TX, int MT, int NT>
+template <typename TX, int MT, int NT, int WN>
 __global__ void __launch_bounds__(kCtThreads, 1)
 gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__restrict__ Y, int ldy,
                           int64_t rows, int64_t rows_per_slab, int D, int which0,
@@ -2193,11 +2201,12 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
     constexpr bool LO = !std::is_same<TX, uint16_t>::value;
     constexpr int kPl = LO ? 2 : 1;               // planes of X
     constexpr int PX = MT + 8, PY = NT + 8;       // LDS row pitches (bf16)
-    constexpr int WN = NT / 64, WM = 8 / WN;      // wavefront grid
+    constexpr int WM = 8 / WN;                    // wavefront grid WM x WN
     constexpr int MTW = MT / 16 / WM;             // m tiles per wavefront
+    constexpr int NTW = NT / 16 / WN;             // n tiles per wavefront
     constexpr int XV = kCtRows * MT / (LO ? 4 : 8) / kCtThreads;  // X pieces per thread
     constexpr int YV = kCtRows * NT / 4 / kCtThreads;             // Y pieces per thread
-    static_assert(XV >= 1 && YV >= 1, "pieces per thread");
+    static_assert(XV >= 1 && YV >= 1 && MTW >= 1 && NTW >= 1, "tile split");
     __shared__ uint16_t xs[2][kPl][kCtRows][PX];
     __shared__ uint16_t ys[2][2][kCtRows][PY];
 
@@ -2211,10 +2220,10 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
     const int64_t r_end = r_begin + rows_per_slab < rows ? r_begin + rows_per_slab : rows;
 
     typedef typename std::conditional<LO, f4, u4>::type xraw_t;
-    xraw_t xv[XV];
-    f4 yv[YV];
+    xraw_t xvs[2][XV];
+    f4 yvs[2][YV];
     constexpr int XCOLS = LO ? MT / 4 : MT / 8;   // pieces per X row
-    auto load = [&](int64_t rb) {
+    auto load = [&](int set, int64_t rb) {
 #pragma unroll
         for (int u = 0; u < XV; ++u) {
             const int e = tid + kCtThreads * u;
@@ -2222,12 +2231,12 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
             const int64_t gr = rb + r;
             if (gr < r_end) {
                 if constexpr (LO)
-                    xv[u] = *reinterpret_cast<const f4 *>(X + gr * ldx + m0 + 4 * c);
+                    xvs[set][u] = *reinterpret_cast<const f4 *>(X + gr * ldx + m0 + 4 * c);
                 else
-                    xv[u] = *reinterpret_cast<const u4 *>(X + gr * ldx + m0 + 8 * c);
+                    xvs[set][u] = *reinterpret_cast<const u4 *>(X + gr * ldx + m0 + 8 * c);
             } else {
-                if constexpr (LO) xv[u] = zero4();
-                else xv[u] = zero_u4();
+                if constexpr (LO) xvs[set][u] = zero4();
+                else xvs[set][u] = zero_u4();
             }
         }
 #pragma unroll
@@ -2235,31 +2244,34 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
             const int e = tid + kCtThreads * u;
             const int r = e / (NT / 4), c = e % (NT / 4);
             const int64_t gr = rb + r;
-            yv[u] = gr < r_end ? *reinterpret_cast<const f4 *>(Y + gr * ldy + n0 + 4 * c) : zero4();
+            yvs[set][u] = gr < r_end ? *reinterpret_cast<const f4 *>(Y + gr * ldy + n0 + 4 * c)
+                                     : zero4();
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int set, int buf) {
 #pragma unroll
         for (int u = 0; u < XV; ++u) {
             const int e = tid + kCtThreads * u;
             const int r = e / XCOLS, c = e % XCOLS;
             if constexpr (LO) {
-                const uint32_t h01 = pack_bf16(xv[u][0], xv[u][1]), h23 = pack_bf16(xv[u][2], xv[u][3]);
-                const uint32_t l01 = pack_bf16(xv[u][0] - bf_lo(h01), xv[u][1] - bf_hi(h01));
-                const uint32_t l23 = pack_bf16(xv[u][2] - bf_lo(h23), xv[u][3] - bf_hi(h23));
+                const f4 x = xvs[set][u];
+                const uint32_t h01 = pack_bf16(x[0], x[1]), h23 = pack_bf16(x[2], x[3]);
+                const uint32_t l01 = pack_bf16(x[0] - bf_lo(h01), x[1] - bf_hi(h01));
+                const uint32_t l23 = pack_bf16(x[2] - bf_lo(h23), x[3] - bf_hi(h23));
                 *reinterpret_cast<uint2 *>(&xs[buf][0][r][4 * c]) = uint2{h01, h23};
                 *reinterpret_cast<uint2 *>(&xs[buf][kPl - 1][r][4 * c]) = uint2{l01, l23};
             } else {
-                *reinterpret_cast<u4 *>(&xs[buf][0][r][8 * c]) = xv[u];
+                *reinterpret_cast<u4 *>(&xs[buf][0][r][8 * c]) = xvs[set][u];
             }
         }
 #pragma unroll
         for (int u = 0; u < YV; ++u) {
             const int e = tid + kCtThreads * u;
             const int r = e / (NT / 4), c = e % (NT / 4);
-            const uint32_t h01 = pack_bf16(yv[u][0], yv[u][1]), h23 = pack_bf16(yv[u][2], yv[u][3]);
-            const uint32_t l01 = pack_bf16(yv[u][0] - bf_lo(h01), yv[u][1] - bf_hi(h01));
-            const uint32_t l23 = pack_bf16(yv[u][2] - bf_lo(h23), yv[u][3] - bf_hi(h23));
+            const f4 y = yvs[set][u];
+            const uint32_t h01 = pack_bf16(y[0], y[1]), h23 = pack_bf16(y[2], y[3]);
+            const uint32_t l01 = pack_bf16(y[0] - bf_lo(h01), y[1] - bf_hi(h01));
+            const uint32_t l23 = pack_bf16(y[2] - bf_lo(h23), y[3] - bf_hi(h23));
             *reinterpret_cast<uint2 *>(&ys[buf][0][r][4 * c]) = uint2{h01, h23};
             *reinterpret_cast<uint2 *>(&ys[buf][1][r][4 * c]) = uint2{l01, l23};
         }
@@ -2271,35 +2283,47 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
         return u4{a.x, a.y, b.x, b.y};
     };
 
-    f4 acc[MTW][4];
+    f4 acc[MTW][NTW];
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+        for (int j = 0; j < NTW; ++j) acc[i][j] = zero4();
 
+    auto contract = [&](int buf) {
+        Split bo[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int c = 16 * (NTW * wn + j);
+            bo[j].hi = operand(&ys[buf][0][0][0], PY, c);
+            bo[j].lo = operand(&ys[buf][1][0][0], PY, c);
+        }
+#pragma unroll
+        for (int i = 0; i < MTW; ++i) {
+            const int c = 16 * (MTW * wm + i);
+            Split ao;
+            ao.hi = operand(&xs[buf][0][0][0], PX, c);
+            ao.lo = LO ? operand(&xs[buf][kPl - 1][0][0], PX, c) : zero_u4();
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[i][j] = mfma3<LO>(ao, bo[j], acc[i][j]);
+        }
+    };
+    // step k: its rows (register set k % 2) go to LDS buffer k % 2, the
+    // barrier publishes them (and closes the reads of step k - 1), the set
+    // takes the rows of step k + 2, and the buffer is contracted.  Rows past
+    // the slab load as zeros.
     if (r_begin < r_end) {
-        load(r_begin);
-        int buf = 0;
-        for (int64_t rb = r_begin; rb < r_end; rb += kCtRows, buf ^= 1) {
-            store(buf);
-            __syncthreads();  // this buffer written; the other one's readers are done
-            if (rb + kCtRows < r_end) load(rb + kCtRows);
-            Split bo[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = 64 * wn + 16 * j;
-                bo[j].hi = operand(&ys[buf][0][0][0], PY, c);
-                bo[j].lo = operand(&ys[buf][1][0][0], PY, c);
-            }
-#pragma unroll
-            for (int i = 0; i < MTW; ++i) {
-                const int c = 16 * (MTW * wm + i);
-                Split ao;
-                ao.hi = operand(&xs[buf][0][0][0], PX, c);
-                ao.lo = LO ? operand(&xs[buf][kPl - 1][0][0], PX, c) : zero_u4();
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma3<LO>(ao, bo[j], acc[i][j]);
-            }
+        load(0, r_begin);
+        load(1, r_begin + kCtRows);
+        for (int64_t rb = r_begin; rb < r_end; rb += 2 * kCtRows) {
+            store(0, 0);
+            __syncthreads();
+            load(0, rb + 2 * kCtRows);
+            contract(0);
+            if (rb + kCtRows >= r_end) break;
+            store(1, 1);
+            __syncthreads();
+            load(1, rb + 3 * kCtRows);
+            contract(1);
         }
     }
     // partial of this slab: lane l holds i = m-tile row 4(l/16) + e, o = l % 16
@@ -2307,8 +2331,8 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int o = n0 + 64 * wn + 16 * j + ln;
+        for (int j = 0; j < NTW; ++j) {
+            const int o = n0 + 16 * (NTW * wn + j) + ln;
             const int which = which0 + o / D, s = o % D;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -2542,23 +2566,24 @@ hipError_t split_launch(const Plan &p, const void *hh, const void *hs2, const fl
     }
     if (e != hipSuccess) return e;
     const int64_t rows = p.B * p.K;
-    const int64_t rps = (rows + p.split_slabs - 1) / p.split_slabs;
+    // slabs of whole 32-row steps
+    const int64_t rps = ((rows + p.split_slabs - 1) / p.split_slabs + kCtRows - 1) / kCtRows * kCtRows;
     const int64_t rpsc = (p.B + p.split_slabs - 1) / p.split_slabs;
     const int sh2 = (int)p.SH2, d = (int)p.D;
     // h_history^T @ [dA | dB]: 2D outputs in tiles of 128
-    hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128>),
+    hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128, 4>),
                        dim3((unsigned)p.split_slabs, (unsigned)(p.SH2 / 256), (unsigned)(2 * p.D / 128)),
                        dim3(kCtThreads), 0, st, static_cast<const TIn *>(hh), sh2,
                        (const float *)ab, 2 * d, rows, rps, d, 0, sh2, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // h_s2^T @ dC: D outputs in tiles of 128, or 64
     if (p.D % 128 == 0)
-        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128>),
+        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128, 4>),
                            dim3((unsigned)p.split_slabs, (unsigned)(p.SH2 / 256), (unsigned)(p.D / 128)),
                            dim3(kCtThreads), 0, st, static_cast<const TIn *>(hs2), sh2,
                            (const float *)cv, d, p.B, rpsc, d, 2, sh2, part);
     else
-        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 64>),
+        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 64, 4>),
                            dim3((unsigned)p.split_slabs, (unsigned)(p.SH2 / 256), (unsigned)(p.D / 64)),
                            dim3(kCtThreads), 0, st, static_cast<const TIn *>(hs2), sh2,
                            (const float *)cv, d, p.B, rpsc, d, 2, sh2, part);

@@ -2182,7 +2182,7 @@ gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 // ---- contraction: part[slab][which0 + o / D][i][o % D] = sum over the
 // slab's rows r of X[r][i] * Y[r][o], for i in [m0, m0 + MT), o in
 // [n0, n0 + NT).  32 rows per step: both tiles are split into bf16 high /
-// low planes in LDS (row-major, rows padded by 8 columns) and read back
+// low planes in LDS (row-major, rows padded by 16 columns) and read back
 // transposed with ds_read_b64_tr_b16, so lane l gets column l % 16 of rows
 // 4(l/16) .. +3 and 16 + 4(l/16) .. +3: the MFMA k index 8(l/16) + e for
 // both operands.  The eight wavefronts form a WM x WN grid over the tile.
@@ -2200,7 +2200,9 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
 {
     constexpr bool LO = !std::is_same<TX, uint16_t>::value;
     constexpr int kPl = LO ? 2 : 1;               // planes of X
-    constexpr int PX = MT + 8, PY = NT + 8;       // LDS row pitches (bf16)
+    // LDS row pitches (bf16): a transposed read takes 32 bytes of each of
+    // four rows per 16 lanes, so rows start 32 bytes apart on the banks
+    constexpr int PX = MT + 16, PY = NT + 16;
     constexpr int WM = 8 / WN;                    // wavefront grid WM x WN
     constexpr int MTW = MT / 16 / WM;             // m tiles per wavefront
     constexpr int NTW = NT / 16 / WN;             // n tiles per wavefront

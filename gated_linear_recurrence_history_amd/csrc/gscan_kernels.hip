@@ -2192,12 +2192,16 @@ gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 constexpr int kCtThreads = 512;
 constexpr int kCtRows = 32;
 
-template <typename TX, int MT, int NT, int WN>
+// WHICH0: the partial the first output column goes to (0: dW_A, then dW_B;
+// 2: dW_C), fixed at compile time so that the two launches are told apart
+// in profiles.
+template <typename TX, int MT, int NT, int WN, int WHICH0>
 __global__ void __launch_bounds__(kCtThreads, 1)
 gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__restrict__ Y, int ldy,
-                          int64_t rows, int64_t rows_per_slab, int D, int which0,
-                          int SH2, float *__restrict__ part)
+                          int64_t rows, int64_t rows_per_slab, int D, int SH2,
+                          float *__restrict__ part)
 {
+    constexpr int which0 = WHICH0;
     constexpr bool LO = !std::is_same<TX, uint16_t>::value;
     constexpr int kPl = LO ? 2 : 1;               // planes of X
     // LDS row pitches (bf16): a transposed read takes 32 bytes of each of
@@ -2573,22 +2577,22 @@ hipError_t split_launch(const Plan &p, const void *hh, const void *hs2, const fl
     const int64_t rpsc = (p.B + p.split_slabs - 1) / p.split_slabs;
     const int sh2 = (int)p.SH2, d = (int)p.D;
     // h_history^T @ [dA | dB]: 2D outputs in tiles of 128
-    hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128, 4>),
+    hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128, 4, 0>),
                        dim3((unsigned)p.split_slabs, (unsigned)(p.SH2 / 256), (unsigned)(2 * p.D / 128)),
                        dim3(kCtThreads), 0, st, static_cast<const TIn *>(hh), sh2,
-                       (const float *)ab, 2 * d, rows, rps, d, 0, sh2, part);
+                       (const float *)ab, 2 * d, rows, rps, d, sh2, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // h_s2^T @ dC: D outputs in tiles of 128, or 64
     if (p.D % 128 == 0)
-        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128, 4>),
+        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 128, 4, 2>),
                            dim3((unsigned)p.split_slabs, (unsigned)(p.SH2 / 256), (unsigned)(p.D / 128)),
                            dim3(kCtThreads), 0, st, static_cast<const TIn *>(hs2), sh2,
-                           (const float *)cv, d, p.B, rpsc, d, 2, sh2, part);
+                           (const float *)cv, d, p.B, rpsc, d, sh2, part);
     else
-        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 64, 4>),
+        hipLaunchKernelGGL((gscan_bwd_contract_kernel<TIn, 256, 64, 4, 2>),
                            dim3((unsigned)p.split_slabs, (unsigned)(p.SH2 / 256), (unsigned)(p.D / 64)),
                            dim3(kCtThreads), 0, st, static_cast<const TIn *>(hs2), sh2,
-                           (const float *)cv, d, p.B, rpsc, d, 2, sh2, part);
+                           (const float *)cv, d, p.B, rpsc, d, sh2, part);
     return hipGetLastError();
 }
 

@@ -101,9 +101,9 @@ def counter_per_dispatch(directory: str, counter: str):
 def write_stats(directory, out_path, command):
     lines = ["rocprofv3 kernel statistics (from its kernel_stats.csv)", "",
              f"command: {command}", "",
-             f"{'kernel':<44} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'share':>7}"]
+             f"{'kernel':<56} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'share':>7}"]
     for name, calls, avg, mn, mx, tot, pct in stats(directory):
-        lines.append(f"{name[:44]:<44} {calls:>6} {avg / 1e3:>9.3f} {mn / 1e3:>9.3f} "
+        lines.append(f"{name[:56]:<56} {calls:>6} {avg / 1e3:>9.3f} {mn / 1e3:>9.3f} "
                      f"{mx / 1e3:>9.3f} {pct:>6.2f}%")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -33,7 +33,10 @@ Fields beyond the headline value:
                     its algorithmic bytes per launch over its average
                     duration; `traffic` is the HBM bytes per launch that
                     rocprofv3 counters measured for the same kernel source
-                    (profiles/traffic_<kernel>_<workload>.txt), else null
+                    (profiles/traffic_<kernel>_<workload>.txt), else null;
+                    where the backward's phase 1 is the split pair (scan
+                    pass, then contraction) the two are one phase: their
+                    summed time and traffic
   cpu_baseline      the fp64 CPU oracle timed on a bounded sample of the
                     same workload on this host's cores
   configs           every named workload (tiny, headline, long K, bf16 big
@@ -413,6 +416,22 @@ def read_ceiling(stream, nbytes=1 << 30, reps=8):
     return nbytes / float(np.median(times[2:])) / 1e9
 
 
+def plan_kernels(w):
+    """(forward kernel, backward phase-1 kernels) the launch plan picks for
+    workload `w`: the library's rule, restated for labelling the bench line."""
+    slices = w.D // 16
+    groups = -(-w.B // 16)
+    fwd = "gscan_fwd_kernel" if groups <= 512 else "gscan_fwd_persist_kernel"
+    if slices >= 2 and (w.K >= 16 or groups <= 512):
+        if any(slices % sv == 0 and sv * (w.SH2 // 32) <= 32 for sv in (4, 2)):
+            fwd = "gscan_fwd_ms_kernel"
+    if (w.SH2 == 512 and w.D % 64 == 0 and w.K in (64, 256) and w.B % (256 // w.K) == 0):
+        return fwd, ("gscan_bwd_scan_kernel", "gscan_bwd_contract_kernel")
+    if (16 % w.K == 0 or w.K in (32, 64)) and w.SH2 <= 256:
+        return fwd, ("gscan_bwd_rows_kernel",)
+    return fwd, ("gscan_bwd_kernel",)
+
+
 def traffic_record(kernel, workload):
     """HBM bytes per launch measured by rocprofv3 for this exact kernel source, or None."""
     from gated_linear_recurrence_history_amd import rocprof_summary as rs
@@ -568,22 +587,23 @@ def main():
 
     # dominant kernel against HBM (its MFMA time, 3 bf16 products per fp32
     # product at the bf16 peak, is far below its HBM time)
+    fname, bnames = plan_kernels(w)
     if k_bwd >= k_fwd:
-        # K dividing 16, or K = 32 or 64, with SH2 <= 256 runs the per-block
-        # backward kernel (the launch plan's rule)
-        rows = (16 % w.K == 0 or w.K in (32, 64)) and w.SH2 <= 256
-        bname = "gscan_bwd_rows_kernel" if rows else "gscan_bwd_kernel"
-        kname, kus, kbytes, kflops = bname, k_bwd, w.bwd_bytes(), w.bwd_flops()
+        # the backward's phase 1: one kernel, or the split pair (scan pass and
+        # contraction, timed together as one phase)
+        kname, kus, kbytes, kflops = "+".join(bnames), k_bwd, w.bwd_bytes(), w.bwd_flops()
     else:
-        kname, kus, kbytes, kflops = "gscan_fwd_kernel", k_fwd, w.fwd_bytes(), w.fwd_flops()
+        bnames = (fname,)
+        kname, kus, kbytes, kflops = fname, k_fwd, w.fwd_bytes(), w.fwd_flops()
     t_hbm_us = kbytes / (HBM_PEAK_GBS * 1e9) * 1e6
     t_mfma_us = SPLIT_PRODUCTS * kflops / (BF16_PEAK_TFLOPS * 1e12) * 1e6
     ach = kbytes / (kus * 1e-6) / 1e9
-    rec = traffic_record(kname, w.name)
+    recs = [traffic_record(k, w.name) for k in bnames]
+    traffic = sum(r["traffic_bytes"] for r in recs) if all(recs) else None
     roof = {"bound": "hbm" if t_hbm_us >= t_mfma_us else "mfma", "achieved": round(ach, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
             "frac_of_read_ceiling": round(ach / rd_gbs, 4),
-            "traffic": rec["traffic_bytes"] if rec else None,
+            "traffic": traffic,
             "kernel": kname, "avg_us": round(kus, 3), "algorithmic_bytes": kbytes,
             "hbm_floor_us": round(t_hbm_us, 3), "mfma_floor_us": round(t_mfma_us, 3)}
 
@@ -615,7 +635,7 @@ def main():
         "step_us": step_us,
         "copy_GBs": round(copy_gbs, 1),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
-        "kernels_us": {"gscan_fwd_kernel": round(k_fwd, 3), "backward_phase1": round(k_bwd, 3),
+        "kernels_us": {"forward": round(k_fwd, 3), "backward_phase1": round(k_bwd, 3),
                        "gscan_reduce_kernel": round(k_red, 3)},
         "roofline": roof,
     }

@@ -25,7 +25,11 @@
  * 16-bit storage).  Everything else is float32; all accumulation is float32.
  *
  * Supported shapes: B >= 1, 1 <= K <= 262144, 64 <= SH2 <= 512 with SH2 % 64 == 0,
- * 16 <= D <= 256 with D % 16 == 0, B*K*SH2 < 2^62.
+ * 16 <= D <= 256 with D % 16 == 0, B*K*SH2 < 2^62.  SH2 stops at 512 because
+ * every kernel keeps its weight slice, split into bf16 hi/lo halves, in the
+ * 160 KiB of LDS for the whole launch: 192 * SH2 bytes per 16 states (96 KiB
+ * at SH2 = 512); SH2 % 64 lets two wavefronts share a row block by halves of
+ * 32-column MFMA units.  Other shapes return GSCAN_ERR_UNSUPPORTED_SHAPE.
  *
  * Pointers: every array pointer is DEVICE memory owned by the caller,
  * 16-byte aligned.  Inputs are read only and must not overlap outputs.  The

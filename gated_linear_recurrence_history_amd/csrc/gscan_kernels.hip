@@ -96,17 +96,31 @@ struct Split {
     u4 hi, lo;
 };
 
+// Low halves of a split pair: bf16(a - hi_a), bf16(b - hi_b) for the pair
+// h = pack_bf16(a, b).  Each remainder is the bf16 dot product -1 * hi + 0 *
+// (the other half) + x: the products are exact and x - hi is representable
+// in fp32 (hi is x rounded to 8 significant bits), so the remainder is exact
+// whatever the dot product's internal rounding, in one instruction instead
+// of unpacking hi and subtracting.  The two selector constants are passed
+// in scalar registers: as an inline constant, (-1, 0) is encoded as the
+// fp32 -1.0 (0xbf800000), which the hardware reads as (0, -1).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t h, float a, float b)
+{
+    uint32_t m0 = 0x0000bf80u, m1 = 0xbf800000u;
+    asm("" : "+s"(m0), "+s"(m1));
+    const bf16x2 hv = __builtin_bit_cast(bf16x2, h);
+    return pack_bf16(
+        __builtin_amdgcn_fdot2_f32_bf16(hv, __builtin_bit_cast(bf16x2, m0), a, false),
+        __builtin_amdgcn_fdot2_f32_bf16(hv, __builtin_bit_cast(bf16x2, m1), b, false));
+}
+
 __device__ __forceinline__ Split split8(const float (&v)[8])
 {
     Split s;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t h = pack_bf16(v[2 * i], v[2 * i + 1]);
-        // opaque, so the low element's high part is taken from the pair
-        // (one shift) instead of being converted a second time
-        asm("" : "+v"(h));
-        s.hi[i] = h;
-        s.lo[i] = pack_bf16(v[2 * i] - bf_lo(h), v[2 * i + 1] - bf_hi(h));
+        s.hi[i] = pack_bf16(v[2 * i], v[2 * i + 1]);
+        s.lo[i] = pack_lo(s.hi[i], v[2 * i], v[2 * i + 1]);
     }
     return s;
 }
@@ -1419,8 +1433,8 @@ template <bool LO>
 __device__ __forceinline__ GradOp grad_op(const f4 &d)
 {
     const uint32_t h01 = pack_bf16(d[0], d[1]), h23 = pack_bf16(d[2], d[3]);
-    const uint32_t l01 = pack_bf16(d[0] - bf_lo(h01), d[1] - bf_hi(h01));
-    const uint32_t l23 = pack_bf16(d[2] - bf_lo(h23), d[3] - bf_hi(h23));
+    const uint32_t l01 = pack_lo(h01, d[0], d[1]);
+    const uint32_t l23 = pack_lo(h23, d[2], d[3]);
     GradOp g;
     if constexpr (LO) {
         g.b1 = u4{h01, h23, h01, h23};
@@ -2262,8 +2276,8 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
             if constexpr (LO) {
                 const f4 x = xvs[set][u];
                 const uint32_t h01 = pack_bf16(x[0], x[1]), h23 = pack_bf16(x[2], x[3]);
-                const uint32_t l01 = pack_bf16(x[0] - bf_lo(h01), x[1] - bf_hi(h01));
-                const uint32_t l23 = pack_bf16(x[2] - bf_lo(h23), x[3] - bf_hi(h23));
+                const uint32_t l01 = pack_lo(h01, x[0], x[1]);
+                const uint32_t l23 = pack_lo(h23, x[2], x[3]);
                 *reinterpret_cast<uint2 *>(&xs[buf][0][r][4 * c]) = uint2{h01, h23};
                 *reinterpret_cast<uint2 *>(&xs[buf][kPl - 1][r][4 * c]) = uint2{l01, l23};
             } else {
@@ -2276,8 +2290,8 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
             const int r = e / (NT / 4), c = e % (NT / 4);
             const f4 y = yvs[set][u];
             const uint32_t h01 = pack_bf16(y[0], y[1]), h23 = pack_bf16(y[2], y[3]);
-            const uint32_t l01 = pack_bf16(y[0] - bf_lo(h01), y[1] - bf_hi(h01));
-            const uint32_t l23 = pack_bf16(y[2] - bf_lo(h23), y[3] - bf_hi(h23));
+            const uint32_t l01 = pack_lo(h01, y[0], y[1]);
+            const uint32_t l23 = pack_lo(h23, y[2], y[3]);
             *reinterpret_cast<uint2 *>(&ys[buf][0][r][4 * c]) = uint2{h01, h23};
             *reinterpret_cast<uint2 *>(&ys[buf][1][r][4 * c]) = uint2{l01, l23};
         }

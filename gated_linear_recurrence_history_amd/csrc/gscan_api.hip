@@ -92,6 +92,11 @@ FullLayout full_layout(const gscan::Plan &p)
 {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     FullLayout f;
+    if (p.fused_dinput()) {  // phase 1 writes the input gradients: partials only
+        f.dab = f.dc = 0;
+        f.bytes = p.ws_bytes;
+        return f;
+    }
     if (p.bwd_split) {  // the split backward's workspace already holds both
         f.dab = p.split_dab;
         f.dc = p.split_dc;
@@ -258,7 +263,8 @@ int gscan_backward_ex(const void *h_history, const void *h_s2, const float *W_A,
     }
     float *part = static_cast<float *>(ws);
     hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
-                                                   d_context, part, nullptr, nullptr, stream);
+                                                   d_context, part, nullptr, nullptr, nullptr,
+                                                   nullptr, stream);
     if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
     if (!workspace) {
         hipError_t f = hipFreeAsync(ws, stream);
@@ -313,16 +319,25 @@ int gscan_backward_full_ex(const void *h_history, const void *h_s2, const float 
     }
     char *base = static_cast<char *>(ws);
     float *part = reinterpret_cast<float *>(base);
-    float *dab = reinterpret_cast<float *>(base + lay.dab);
-    float *dc = reinterpret_cast<float *>(base + lay.dc);
-    hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
-                                                   d_context, part, dab, dc, stream);
-    if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
-    if (e == hipSuccess && !plan.adjoints_final())
-        e = gscan::launch_adjoint(plan, dab, dc, d_context, a_shift, stream);
-    if (e == hipSuccess)
-        e = gscan::launch_dinput(dab, W_A, W_B, D, 2 * D, SH2, B * K, d_h_history, stream);
-    if (e == hipSuccess) e = gscan::launch_dinput(dc, W_C, nullptr, D, D, SH2, B, d_h_s2, stream);
+    hipError_t e;
+    if (plan.fused_dinput()) {
+        // phase 1 writes d_h_history and d_h_s2 itself
+        e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
+                                            d_context, part, nullptr, nullptr, d_h_history,
+                                            d_h_s2, stream);
+        if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
+    } else {
+        float *dab = reinterpret_cast<float *>(base + lay.dab);
+        float *dc = reinterpret_cast<float *>(base + lay.dc);
+        e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
+                                            d_context, part, dab, dc, nullptr, nullptr, stream);
+        if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
+        if (e == hipSuccess && !plan.adjoints_final())
+            e = gscan::launch_adjoint(plan, dab, dc, d_context, a_shift, stream);
+        if (e == hipSuccess)
+            e = gscan::launch_dinput(dab, W_A, W_B, D, 2 * D, SH2, B * K, d_h_history, stream);
+        if (e == hipSuccess) e = gscan::launch_dinput(dc, W_C, nullptr, D, D, SH2, B, d_h_s2, stream);
+    }
     if (!workspace) {
         hipError_t f = hipFreeAsync(ws, stream);
         if (e == hipSuccess) e = f;
@@ -392,7 +407,7 @@ int gscan_backward_partials(const void *h_history, const void *h_s2, const float
     clear_stale_error();
     hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
                                                    d_context, static_cast<float *>(workspace),
-                                                   nullptr, nullptr, stream);
+                                                   nullptr, nullptr, nullptr, nullptr, stream);
     if (e != hipSuccess)
         return fail(GSCAN_ERR_HIP, "backward phase 1 launch failed: %s", hipGetErrorString(e));
     g_last_error[0] = '\0';
@@ -447,7 +462,8 @@ int gscan_backward_noalloc(const void *h_history, const void *h_s2, const float 
     // scratch needs to start at zero
     float *part = static_cast<float *>(ws);
     hipError_t e = gscan::launch_backward_partials(plan, h_history, h_s2, W_A, W_B, W_C, a_shift,
-                                                   d_context, part, nullptr, nullptr, stream);
+                                                   d_context, part, nullptr, nullptr, nullptr,
+                                                   nullptr, stream);
     if (e == hipSuccess) e = gscan::launch_backward_reduce(plan, part, dW_A, dW_B, dW_C, stream);
     if (e != hipSuccess)
         return fail(GSCAN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));

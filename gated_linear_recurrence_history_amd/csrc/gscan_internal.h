@@ -45,6 +45,9 @@ struct Plan {
     size_t ws_bytes = 0;    // the backward's workspace (partials, and the split pass's adjoints)
     // phase 1 leaves the final dL/dA | dL/dB and dL/dC (not projections)
     bool adjoints_final() const { return bwd_rows_kernel || bwd_split; }
+    // phase 1 writes the input gradients itself (the per-block kernel with
+    // one 16-state slice holds every state of a row)
+    bool fused_dinput() const { return bwd_rows_kernel && slices == 1; }
 };
 
 // Where the forward writes context[b][s]: the context output (null: not
@@ -66,12 +69,15 @@ hipError_t launch_forward(const Plan &p, const void *h_history, const void *h_s2
 // Phase 1: per-workgroup weight-gradient partials into `partials`.  When
 // `dab` / `dc` are not null they receive, for the input gradients, either
 // the final dL/dA | dL/dB per row ([B*K][2D]) and dL/dC per sample ([B][D])
-// (p.bwd_rows_kernel), or the projections A | Bv and C in the same places,
-// which launch_adjoint then turns into those adjoints.
+// (p.adjoints_final()), or the projections A | Bv and C in the same places,
+// which launch_adjoint then turns into those adjoints.  When `dh` / `dhs2`
+// are not null (only where p.fused_dinput(); dab and dc then null) phase 1
+// writes d_h_history [B*K][SH2] and d_h_s2 [B][SH2] itself.
 hipError_t launch_backward_partials(const Plan &p, const void *h_history, const void *h_s2,
                                     const float *W_A, const float *W_B, const float *W_C,
                                     float a_shift, const float *d_context, float *partials,
-                                    float *dab, float *dc, hipStream_t stream);
+                                    float *dab, float *dc, float *dh, float *dhs2,
+                                    hipStream_t stream);
 
 // In place: A | Bv -> dL/dA | dL/dB per row, C -> dL/dC per sample.
 hipError_t launch_adjoint(const Plan &p, float *ab, float *cv, const float *d_context,

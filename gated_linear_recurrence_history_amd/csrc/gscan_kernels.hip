@@ -1464,16 +1464,58 @@ __device__ __forceinline__ f4 contract_op(const u4 &a, const GradOp &g, f4 acc)
 constexpr int kWaves2 = 8;
 constexpr int kThreads2 = kWave * kWaves2;
 
+// Input gradients in the same pass (DIN, one 16-state slice: D = 16).  After
+// the contraction each wavefront forms, for its block's 16 rows and its half
+// of the columns, d_h_history = [dL/dA | dL/dBv] [W_A | W_B]^T, and at a
+// group's end d_h_s2 = dL/dC W_C^T for its 32-column unit: per 16-column
+// tile, the transposed product (W tile rows i, k = the 32 states of A and B)
+// x ([dA | dB] with k = state, column = row), three bf16 MFMAs with both
+// operands split.  The weight operand comes from the staged image by
+// transposed reads (lane i, four states of row i per read); [dA | dB] is
+// written split to the wavefront's transposition tile as [plane][state][row]
+// and read back the same way.  A lane ends with four consecutive columns of
+// one row: one 128-bit store.
+//
+// Transposed read of four consecutive states n0 .. n0+3 of the weight image
+// rows i0 .. i0+15 (i0 % 16 == 0) of weight w, plane p: lane i of a 16-lane
+// group gets W_w[i0 + i][n0 + j], j = 0..3.  Image entry (q, w, p, lane L)
+// holds W_w[32q + 8(L/16) + e][L % 16], e = 0..7, so lane 4j + m of the group
+// addresses the 8-byte half m % 2 of entry L = n0 + j + 16((i0 % 32) / 8 +
+// m / 2): rows i0 + 4m .. +3 of state n0 + j.
+__device__ __forceinline__ uint2 wimage_tr(const u4 *Wl, int q, int w, int p, int i0mod32, int n0,
+                                           int pl)
+{
+    const int m = pl & 3, j = pl >> 2;
+    const int L = n0 + j + 16 * ((i0mod32 >> 3) + (m >> 1));
+    const char *b = reinterpret_cast<const char *>(Wl + ((q * 3 + w) * 2 + p) * kWave + L);
+    return read_tr(reinterpret_cast<const uint16_t *>(b + 8 * (m & 1)));
+}
+
+// 128-bit stores through a buffer resource of `bytes` bytes at `base`: the
+// hardware drops a store at an offset past the end, so the stores for rows
+// past the batch need no branch, and the compiler's waits on the memory
+// counter (which stores share with the row loads) count them exactly.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void store_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, const f4 &v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, (int)off, 0, 0);
+}
+
 // KT: the scan length when fixed at compile time (the index arithmetic and
 // the branches on K then fold), 0 to take it from the argument.
-template <typename TIn, int NQ, int KT>
+template <typename TIn, int NQ, int KT, bool DIN>
 __global__ void __launch_bounds__(kThreads2, 1)
 gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                       const float *__restrict__ WA, const float *__restrict__ WB,
                       const float *__restrict__ WC, int64_t B, int Kin, int D, int slices,
                       int64_t groups, int64_t nrows, float a_shift,
                       const float *__restrict__ dctx, float *__restrict__ part,
-                      float *__restrict__ dab_out, float *__restrict__ dc_out)
+                      float *__restrict__ dab_out, float *__restrict__ dc_out,
+                      float *__restrict__ dh_out, float *__restrict__ dhs2_out)
 {
     const int K = KT ? KT : Kin;
     constexpr int SH2 = NQ * 32;
@@ -1492,7 +1534,11 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     // the end, as the cross-wavefront sums
     constexpr int kPitch = HC + 8;
     constexpr int kPlanes = LO ? 2 : 1;
-    constexpr int kStage = kWaves2 * kPlanes * 16 * kPitch * 2;
+    // per-wavefront tile in bf16 elements (DIN: at least the [2][32][16] tile
+    // of the split [dA | dB])
+    constexpr int kTileE = kPlanes * 16 * kPitch;
+    constexpr int kTile = DIN && kTileE < 1024 ? 1024 : kTileE;
+    constexpr int kStage = kWaves2 * kTile * 2;
     constexpr int kRed = 2 * 2 * SH2 * 16 * 4;
     constexpr int kRaw = raw_rows_of(NQ) * 16 * 4;
     constexpr int kMem = kStage > kRed ? (kStage > kRaw ? kStage : kRaw) : (kRed > kRaw ? kRed : kRaw);
@@ -1509,7 +1555,7 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     const int kg = lane >> 4, ln = lane & 15;
     const int blk = wave & 3, half = wave >> 2;
     const int kshift = __builtin_ctz((unsigned)K);  // K: a power of two <= 16, or 32, 64
-    uint16_t *const tile = reinterpret_cast<uint16_t *>(stage_mem) + wave * kPlanes * 16 * kPitch;
+    uint16_t *const tile = reinterpret_cast<uint16_t *>(stage_mem) + wave * kTile;
     uint16_t *const hst = reinterpret_cast<uint16_t *>(hst_mem) + wave * kPlanes * 16 * 32;
 
     f4 accA[NQ], accB[NQ], accC[2];  // i-tiles of this half; dW_C unit `wave`
@@ -1778,7 +1824,7 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             if (j > 0) m_in = tj[j] == 0 ? lprev[j] : gt * m_in;
         }
 
-        if (dab_out && half == 0) {
+        if (!DIN && dab_out && half == 0) {
             // dL/dA | dL/dB of this block's rows, for the input gradients
             float *o = dab_out + (cur.g * kGroupSamples * K + lr0 + 4 * kg) * (int64_t)(2 * D) + s0 + ln;
 #pragma unroll
@@ -1806,9 +1852,47 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             if (tl % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounded read-ahead
         }
 
+        if constexpr (DIN) {
+            // [dA | dB] split into the tile as [plane][state][row] (32-byte
+            // state rows; the contraction's reads of the tile come first in
+            // this wavefront's LDS order), then read back transposed: lane l
+            // gets row l % 16 of states 8(l/16) .. +7 (dA for l < 32, dB after)
+            const uint32_t a01 = pack_bf16(dA4[0], dA4[1]), a23 = pack_bf16(dA4[2], dA4[3]);
+            const uint32_t b01 = pack_bf16(dB4[0], dB4[1]), b23 = pack_bf16(dB4[2], dB4[3]);
+            *reinterpret_cast<uint2 *>(tile + ln * 16 + 4 * kg) = uint2{a01, a23};
+            *reinterpret_cast<uint2 *>(tile + (16 + ln) * 16 + 4 * kg) = uint2{b01, b23};
+            *reinterpret_cast<uint2 *>(tile + 512 + ln * 16 + 4 * kg) =
+                uint2{pack_lo(a01, dA4[0], dA4[1]), pack_lo(a23, dA4[2], dA4[3])};
+            *reinterpret_cast<uint2 *>(tile + 512 + (16 + ln) * 16 + 4 * kg) =
+                uint2{pack_lo(b01, dB4[0], dB4[1]), pack_lo(b23, dB4[2], dB4[3])};
+            const uint16_t *const dp = tile + (8 * kg + (ln >> 2)) * 16 + 4 * (ln & 3);
+            const uint2 h0 = read_tr(dp), h1 = read_tr(dp + 64);
+            const uint2 l0 = read_tr(dp + 512), l1 = read_tr(dp + 576);
+            const u4 dH = {h0.x, h0.y, h1.x, h1.y}, dL = {l0.x, l0.y, l1.x, l1.y};
+            const int wsel = kg >> 1, n0 = 8 * (kg & 1);
+            // the group's rows; rows past the batch fall past the resource
+            const __amdgpu_buffer_rsrc_t orsc =
+                out_rsrc(dh_out + cur.g * kGroupSamples * K * (int64_t)SH2, (uint32_t)(NR * SH2 * 4));
+            const uint32_t ooff = ((uint32_t)(lr0 + ln) * SH2 + HC * half + 4 * kg) * 4;
+#pragma unroll
+            for (int t = 0; t < NQ; ++t) {
+                const int q = half * NH + t / 2;
+                const uint2 wh0 = wimage_tr(Wl, q, wsel, 0, 16 * (t & 1), n0, ln);
+                const uint2 wh1 = wimage_tr(Wl, q, wsel, 0, 16 * (t & 1), n0 + 4, ln);
+                const uint2 wl0 = wimage_tr(Wl, q, wsel, 1, 16 * (t & 1), n0, ln);
+                const uint2 wl1 = wimage_tr(Wl, q, wsel, 1, 16 * (t & 1), n0 + 4, ln);
+                const u4 wH = {wh0.x, wh0.y, wh1.x, wh1.y}, wL = {wl0.x, wl0.y, wl1.x, wl1.y};
+                f4 o = mfma_bf(wH, dL, zero4());
+                o = mfma_bf(wL, dH, o);
+                o = mfma_bf(wH, dH, o);
+                store_b128(orsc, ooff + 64 * t, o);
+                if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounded read-ahead
+            }
+        }
+
         if (c == nch - 1) {
             __syncthreads();  // dL/dC of the whole group written
-            if (dc_out && tid < 256) {
+            if (!DIN && dc_out && tid < 256) {
                 const int bl = tid >> 4, s = tid & 15;
                 if (bl < nb) dc_out[(cur.g * kGroupSamples + bl) * D + s0 + s] = dCl[bl][s];
             }
@@ -1833,6 +1917,34 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                     av = u4{h.x, h.y, h.x, h.y};
                 }
                 accC[t] = contract_op<LO>(av, gC, accC[t]);
+            }
+            if constexpr (DIN) {
+                // d_h_s2 of unit `wave`: W_C tile (k = states 0..15, zero
+                // above) x dL/dC (k = state, column = sample)
+                if (wave < NQ) {
+                    const bool kv = kg < 2;
+                    const float *const dcr = &dCl[ln][8 * (kg & 1)];
+                    float dv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dv[e] = kv ? dcr[e] : 0.f;
+                    const Split ds = split8(dv);
+                    const __amdgpu_buffer_rsrc_t orsc =
+                        out_rsrc(dhs2_out + cur.g * kGroupSamples * (int64_t)SH2, (uint32_t)(nb * SH2 * 4));
+                    const uint32_t ooff = ((uint32_t)ln * SH2 + 32 * wave + 4 * kg) * 4;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const uint2 wh0 = wimage_tr(Wl, wave, 2, 0, 16 * t, 8 * (kg & 1), ln);
+                        const uint2 wh1 = wimage_tr(Wl, wave, 2, 0, 16 * t, 8 * (kg & 1) + 4, ln);
+                        const uint2 wl0 = wimage_tr(Wl, wave, 2, 1, 16 * t, 8 * (kg & 1), ln);
+                        const uint2 wl1 = wimage_tr(Wl, wave, 2, 1, 16 * t, 8 * (kg & 1) + 4, ln);
+                        const u4 wH = kv ? u4{wh0.x, wh0.y, wh1.x, wh1.y} : zero_u4();
+                        const u4 wL = kv ? u4{wl0.x, wl0.y, wl1.x, wl1.y} : zero_u4();
+                        f4 o = mfma_bf(wH, ds.lo, zero4());
+                        o = mfma_bf(wL, ds.hi, o);
+                        o = mfma_bf(wH, ds.hi, o);
+                        store_b128(orsc, ooff + 64 * t, o);
+                    }
+                }
             }
             // the next group's C partials and d_context: every reader of this
             // group's values (in the walks) is past the barrier above; dCl is
@@ -2613,8 +2725,9 @@ hipError_t split_launch(const Plan &p, const void *hh, const void *hs2, const fl
 template <typename TIn, int NQ>
 hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const float *WA,
                       const float *WB, const float *WC, float a_shift, const float *dctx,
-                      float *part, float *dab, float *dc, hipStream_t st)
+                      float *part, float *dab, float *dc, float *dh, float *dhs2, hipStream_t st)
 {
+    if (dh && !p.fused_dinput()) return hipErrorInvalidValue;
     if (p.bwd_split) return split_launch<TIn, NQ>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, st);
     const bool aligned = 16 % p.K == 0;
     if constexpr (NQ <= 8) {
@@ -2623,13 +2736,18 @@ hipError_t bwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
                 hipLaunchKernelGGL(kern, dim3((unsigned)p.bwd_grid), dim3(kThreads2), 0, st,
                                    static_cast<const TIn *>(hh), static_cast<const TIn *>(hs2), WA,
                                    WB, WC, p.B, (int)p.K, (int)p.D, p.slices, p.groups,
-                                   p.bwd_rows, a_shift, dctx, part, dab, dc);
+                                   p.bwd_rows, a_shift, dctx, part, dab, dc, dh, dhs2);
                 return hipGetLastError();
             };
+            // the input gradients in the same pass (one state slice)
+            if (dh) {
+                if (p.K == 8) return go(gscan_bwd_rows_kernel<TIn, NQ, 8, true>);
+                return go(gscan_bwd_rows_kernel<TIn, NQ, 0, true>);
+            }
             // K = 8 (the spec's history length) and K = 64 run with K folded in
-            if (p.K == 8) return go(gscan_bwd_rows_kernel<TIn, NQ, 8>);
-            if (p.K == 64) return go(gscan_bwd_rows_kernel<TIn, NQ, 64>);
-            return go(gscan_bwd_rows_kernel<TIn, NQ, 0>);
+            if (p.K == 8) return go(gscan_bwd_rows_kernel<TIn, NQ, 8, false>);
+            if (p.K == 64) return go(gscan_bwd_rows_kernel<TIn, NQ, 64, false>);
+            return go(gscan_bwd_rows_kernel<TIn, NQ, 0, false>);
         }
     }
     // K dividing 16 with NQ <= 8 always takes the per-block kernel above
@@ -2669,17 +2787,17 @@ hipError_t fwd_by_nq(const Plan &p, const void *hh, const void *hs2, const float
 template <typename TIn>
 hipError_t bwd_by_nq(const Plan &p, const void *hh, const void *hs2, const float *WA,
                      const float *WB, const float *WC, float a, const float *dctx, float *part,
-                     float *dab, float *dc, hipStream_t st)
+                     float *dab, float *dc, float *dh, float *dhs2, hipStream_t st)
 {
     switch (p.nq) {
-    case 2: return bwd_launch<TIn, 2>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
-    case 4: return bwd_launch<TIn, 4>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
-    case 6: return bwd_launch<TIn, 6>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
-    case 8: return bwd_launch<TIn, 8>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
-    case 10: return bwd_launch<TIn, 10>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
-    case 12: return bwd_launch<TIn, 12>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
-    case 14: return bwd_launch<TIn, 14>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
-    case 16: return bwd_launch<TIn, 16>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, st);
+    case 2: return bwd_launch<TIn, 2>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, dh, dhs2, st);
+    case 4: return bwd_launch<TIn, 4>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, dh, dhs2, st);
+    case 6: return bwd_launch<TIn, 6>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, dh, dhs2, st);
+    case 8: return bwd_launch<TIn, 8>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, dh, dhs2, st);
+    case 10: return bwd_launch<TIn, 10>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, dh, dhs2, st);
+    case 12: return bwd_launch<TIn, 12>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, dh, dhs2, st);
+    case 14: return bwd_launch<TIn, 14>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, dh, dhs2, st);
+    case 16: return bwd_launch<TIn, 16>(p, hh, hs2, WA, WB, WC, a, dctx, part, dab, dc, dh, dhs2, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -2770,11 +2888,11 @@ hipError_t launch_forward(const Plan &p, const void *hh, const void *hs2, const 
 hipError_t launch_backward_partials(const Plan &p, const void *hh, const void *hs2,
                                     const float *WA, const float *WB, const float *WC,
                                     float a_shift, const float *dctx, float *part, float *dab,
-                                    float *dc, hipStream_t st)
+                                    float *dc, float *dh, float *dhs2, hipStream_t st)
 {
     return p.dtype == 1
-               ? bwd_by_nq<uint16_t>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, st)
-               : bwd_by_nq<float>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, st);
+               ? bwd_by_nq<uint16_t>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, dh, dhs2, st)
+               : bwd_by_nq<float>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, dh, dhs2, st);
 }
 
 hipError_t launch_adjoint(const Plan &p, float *ab, float *cv, const float *dctx, float a_shift,

@@ -180,8 +180,10 @@ int gscan_backward_reduce(const void *workspace, size_t workspace_bytes,
  * are fp32 row-major for either input dtype, caller-owned, 16-byte aligned,
  * overwritten.  workspace: at least gscan_backward_full_workspace_bytes(),
  * 256-byte aligned, or NULL to allocate stream-ordered; it holds the
- * weight-gradient partials, dL/dA | dL/dB per row and dL/dC per sample;
- * contents on entry are ignored.  Errors as for gscan_backward_ex.
+ * weight-gradient partials and, for shapes whose backward does not form the
+ * input gradients in the same pass (the size query accounts for this),
+ * dL/dA | dL/dB per row and dL/dC per sample; contents on entry are
+ * ignored.  Errors as for gscan_backward_ex.
  */
 int gscan_backward_full_ex(const void *h_history, const void *h_s2,
                            const float *W_A, const float *W_B, const float *W_C,

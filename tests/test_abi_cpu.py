@@ -131,15 +131,25 @@ def _split_path(B, K, SH2, D):
     return SH2 == 512 and D % 64 == 0 and K in (64, 256) and B % (256 // K) == 0
 
 
+def _fused_path(B, K, SH2, D):
+    """Shapes whose per-block backward writes the input gradients itself (one
+    16-state slice; K dividing 16, or 32, 64; SH2 <= 256): no adjoints in the
+    workspace."""
+    return D == 16 and (16 % K == 0 or K in (32, 64)) and SH2 <= 256
+
+
 def test_backward_full_workspace_bytes(lib):
     # partials, then dL/dA | dL/dB per row and dL/dC per sample
-    for cfg in wl.WORKLOADS:
-        dt = 1 if cfg.in_dtype == "bf16" else 0
-        part = lib.gscan_backward_workspace_bytes(cfg.B, cfg.K, cfg.SH2, cfg.D, dt)
-        full = lib.gscan_backward_full_workspace_bytes(cfg.B, cfg.K, cfg.SH2, cfg.D, dt)
-        extra = 4 * (cfg.B * cfg.K * 2 * cfg.D + cfg.B * cfg.D)
-        if _split_path(cfg.B, cfg.K, cfg.SH2, cfg.D):
+    shapes = [(c.B, c.K, c.SH2, c.D, 1 if c.in_dtype == "bf16" else 0) for c in wl.WORKLOADS]
+    shapes += [(37, 5, 192, 32, 0), (20, 24, 256, 16, 0), (9, 64, 64, 16, 1), (33, 8, 512, 16, 0)]
+    for B, K, SH2, D, dt in shapes:
+        part = lib.gscan_backward_workspace_bytes(B, K, SH2, D, dt)
+        full = lib.gscan_backward_full_workspace_bytes(B, K, SH2, D, dt)
+        extra = 4 * (B * K * 2 * D + B * D)
+        if _split_path(B, K, SH2, D):
             assert full == part >= extra
+        elif _fused_path(B, K, SH2, D):
+            assert full == part > 0
         else:
             assert part + extra <= full <= part + extra + 512
     assert lib.gscan_backward_full_workspace_bytes(64, 8, 100, 16, 0) == 0

@@ -36,14 +36,32 @@ SHAPES = [
     (70, 2, 256, 16, "f32", 0.0),
     (21, 32, 128, 32, "f32", -1.0),   # samples of 2 blocks (per-block kernel)
     (9, 64, 64, 16, "bf16", 0.5),     # samples of 4 blocks
+    # D = 16 with the per-block kernel: the input gradients come out of the
+    # backward pass itself (ragged groups, every SH2 it takes, K folded in or not)
+    (37, 16, 256, 16, "f32", 1.0),
+    (13, 32, 128, 16, "f32", -2.0),
+    (29, 4, 128, 16, "f32", -1.0),
+    (1000, 8, 192, 16, "bf16", 0.25),
+    (19, 8, 64, 16, "f32", 3.0),
     (8, 64, 512, 64, "f32", 1.0),     # split backward: adjoints straight from the scan pass
     (2, 256, 512, 128, "bf16", -0.5),
 ]
 
 
+def _nan_outs(t, K):
+    """NaN-filled output tensors, so an element a call leaves unwritten fails
+    the comparison."""
+    SH2, D = t["W_A"].shape
+    B = t["h_s2"].shape[0]
+    dev = t["W_A"].device
+    return tuple(torch.full(sh, float("nan"), dtype=torch.float32, device=dev)
+                 for sh in [(SH2, D)] * 3 + [(B * K, SH2), (B, SH2)])
+
+
 def _full(t, K, a, d=None):
     d = t["d_context"] if d is None else d
-    out = gs.backward_full(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], K, d, a)
+    out = _nan_outs(t, K)
+    gs.backward_full(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], K, d, a, out=out)
     torch.cuda.synchronize()
     return tuple(o.cpu().numpy() for o in out)
 
@@ -81,10 +99,11 @@ def test_input_grad_full_size(name):
     print(f"case input grads full {w.name} B={w.B} K={w.K} SH2={w.SH2} D={w.D}", flush=True)
     x = synth.make_inputs(w)
     t = device_inputs(x)
-    out = gs.backward_full(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K,
-                           t["d_context"], w.a_shift)
+    out = _nan_outs(t, w.K)
+    gs.backward_full(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K,
+                     t["d_context"], w.a_shift, out=out)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(out[3]).all())
+    assert bool(torch.isfinite(out[3]).all()) and bool(torch.isfinite(out[4]).all())
     got_dhs = out[4].cpu().numpy()
     if w.name != "wide_fp32":
         got_dh = out[3].cpu().numpy()

@@ -63,9 +63,10 @@ Fields beyond the headline value:
 
 The matrix products run on bf16 MFMA with fp32 operands split into a high
 and a low bf16 part (three products per fp32 product, fp32 accumulation;
-`dtype` says so), so the MFMA time of a pass is at most 3 x its fp32 flops /
-2.5 PFLOP/s -- well under its HBM time: every pass is bounded by HBM
-bandwidth.
+`dtype` says so), so the MFMA time of a pass is at least 3 x its fp32 flops
+/ 2.5 PFLOP/s.  At the headline shape that is well under its HBM time; the
+long-K and wide workloads are bounded by the matrix cores instead (the
+roofline's `bound` says which floor is higher).
 """
 import argparse
 import json
@@ -425,7 +426,10 @@ def plan_kernels(w):
     if slices >= 2 and (w.K >= 16 or groups <= 512):
         if any(slices % sv == 0 and sv * (w.SH2 // 32) <= 32 for sv in (4, 2)):
             fwd = "gscan_fwd_ms_kernel"
-    if (w.SH2 == 512 and w.D % 64 == 0 and w.K in (64, 256) and w.B % (256 // w.K) == 0):
+    tiles = w.K in (64, 256) and w.B % (256 // w.K) == 0 and w.D % 32 == 0
+    if tiles and w.SH2 == 512:
+        fwd = "gscan_fwd_tile_kernel"
+    if tiles and w.SH2 == 512 and w.D % 64 == 0:
         return fwd, ("gscan_bwd_scan_kernel", "gscan_bwd_contract_kernel")
     if (16 % w.K == 0 or w.K in (32, 64)) and w.SH2 <= 256:
         return fwd, ("gscan_bwd_rows_kernel",)

@@ -39,6 +39,7 @@ struct Plan {
     // workspace holds the slab partials, dL/dA | dL/dB per row at split_dab
     // and dL/dC per sample at split_dc (byte offsets)
     bool bwd_split = false;
+    bool fwd_tile = false;  // forward over the split backward's tiles (gscan_fwd_tile_kernel)
     int64_t split_slabs = 0;
     int64_t ps_grid = 0;
     size_t split_dab = 0, split_dc = 0;

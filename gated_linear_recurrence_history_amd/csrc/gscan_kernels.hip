@@ -2110,13 +2110,16 @@ __device__ __forceinline__ void ps_decode(int nsg, int &sg, int64_t &tile0, int6
     tstride = gridDim.x / nsg;
 }
 
-template <typename TIn, int NQ, int KT>
-__global__ void __launch_bounds__(kPsThreads, 1)
-gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
-                      const float *__restrict__ WA, const float *__restrict__ WB,
-                      const float *__restrict__ WC, int64_t ntiles, int D, float a_shift,
-                      const float *__restrict__ dctx, float *__restrict__ dab,
-                      float *__restrict__ dcv)
+// FWD: the forward over the same tiles (projection and forward scan only):
+// context = C * x_K at each sample's last row into `out`; no adjoints.
+template <typename TIn, int NQ, int KT, bool FWD>
+__device__ __forceinline__ void scan_tiles(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
+                                           const float *__restrict__ WA,
+                                           const float *__restrict__ WB,
+                                           const float *__restrict__ WC, int64_t ntiles, int D,
+                                           float a_shift, const float *__restrict__ dctx,
+                                           float *__restrict__ dab, float *__restrict__ dcv,
+                                           const CtxOut &out)
 {
     constexpr int SH2 = NQ * 32;
     constexpr int S = 2;
@@ -2246,7 +2249,7 @@ gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                 const Aff w = compose(tot[sl][1], tot[sl][0]);
                 fmap[par][wave][sl][0][ln] = w.m;
                 fmap[par][wave][sl][1][ln] = w.c;
-                gprod[par][wave][sl][ln] = gall[sl][0] * gall[sl][1];
+                if (!FWD) gprod[par][wave][sl][ln] = gall[sl][0] * gall[sl][1];
             }
         }
         __syncthreads();
@@ -2257,9 +2260,27 @@ gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 #pragma unroll
             for (int p = 0; p < 16; ++p) c += credp[p][j][s];
             cl[par][j][s] = c;
-            dcl[par][j][s] = dctx[(bt + j) * D + s0 + s];
+            if (!FWD) dcl[par][j][s] = dctx[(bt + j) * D + s0 + s];
         }
         __syncthreads();
+
+        if constexpr (FWD) {
+            // the forward walk of the sample's last wavefront, last lane
+            // group: x_K, and context = C * x_K
+            const int sj = wave / WPS, w0 = sj * WPS;
+            if (wave == w0 + WPS - 1 && kg == 3) {
+#pragma unroll
+                for (int sl = 0; sl < S; ++sl) {
+                    const int st = 16 * sl + ln;
+                    float xin = 0.f;
+                    for (int w2 = w0; w2 < wave; ++w2)
+                        xin = fmap[par][w2][sl][0][ln] * xin + fmap[par][w2][sl][1][ln];
+                    const float x = apply(tot[sl][1], apply(tot[sl][0], xin));
+                    put_context(out, bt + sj, D, s0 + st, cl[par][sj][st] * x);
+                }
+            }
+            continue;
+        }
 
         // ---- cross-wavefront folds, walks, adjoints
         const int sj = wave / WPS;            // sample of this wavefront in the tile
@@ -2303,6 +2324,31 @@ gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             }
         }
     }
+}
+
+template <typename TIn, int NQ, int KT>
+__global__ void __launch_bounds__(kPsThreads, 1)
+gscan_bwd_scan_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
+                      const float *__restrict__ WA, const float *__restrict__ WB,
+                      const float *__restrict__ WC, int64_t ntiles, int D, float a_shift,
+                      const float *__restrict__ dctx, float *__restrict__ dab,
+                      float *__restrict__ dcv)
+{
+    scan_tiles<TIn, NQ, KT, false>(hh, hs2, WA, WB, WC, ntiles, D, a_shift, dctx, dab, dcv,
+                                   CtxOut{});
+}
+
+// The forward over 256-row tiles of whole samples, 32 states per workgroup:
+// the scan pass's projection and forward scan, ending in the context.
+template <typename TIn, int NQ, int KT>
+__global__ void __launch_bounds__(kPsThreads, 1)
+gscan_fwd_tile_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
+                      const float *__restrict__ WA, const float *__restrict__ WB,
+                      const float *__restrict__ WC, int64_t ntiles, int D, float a_shift,
+                      CtxOut out)
+{
+    scan_tiles<TIn, NQ, KT, true>(hh, hs2, WA, WB, WC, ntiles, D, a_shift, nullptr, nullptr,
+                                  nullptr, out);
 }
 
 // ---- contraction: part[slab][which0 + o / D][i][o % D] = sum over the
@@ -2643,6 +2689,20 @@ hipError_t fwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
                       const float *WB, const float *WC, float a_shift, const CtxOut &ctx,
                       hipStream_t st)
 {
+    if (p.fwd_tile) {
+        const int64_t ntiles = p.B * p.K / kPsRows;
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)p.ps_grid), dim3(kPsThreads), 0, st,
+                               static_cast<const TIn *>(hh), static_cast<const TIn *>(hs2), WA,
+                               WB, WC, ntiles, (int)p.D, a_shift, ctx);
+            return hipGetLastError();
+        };
+        if constexpr (NQ == 8 || NQ == 16) {
+            if (p.K == 64) return go(gscan_fwd_tile_kernel<TIn, NQ, 64>);
+            if (p.K == 256) return go(gscan_fwd_tile_kernel<TIn, NQ, 256>);
+        }
+        return hipErrorInvalidValue;
+    }
     if (p.fwd_ms == 4) {
         if constexpr (4 * NQ <= 32) {
             hipLaunchKernelGGL((gscan_fwd_ms_kernel<TIn, NQ, 4>), dim3((unsigned)p.fwd_grid),
@@ -2853,14 +2913,21 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
     // kernel's LDS budget) when whole samples fill 256-row tiles (K = 64 or
     // 256 compiled) and the states come in groups of 64
     const int64_t ns = K > 0 && kPsRows % K == 0 ? kPsRows / K : 0;
-    if (SH2 == 512 && D % 64 == 0 && (K == 64 || K == 256) && ns > 0 && B % ns == 0) {
-        q.bwd_split = true;
-        q.bwd_rows_kernel = false;
+    const bool tiles = (K == 64 || K == 256) && ns > 0 && B % ns == 0 && D % kPsStates == 0;
+    if (tiles) {
+        // persistent grid over the 256-row tiles, D / 32 state groups per tile
         const int64_t ntiles = B * K / kPsRows;
         const int64_t nsg = D / kPsStates;
         const int64_t cap = 256 / (8 * nsg) * (8 * nsg);
         const int64_t want = (ntiles + 7) / 8 * 8 * nsg;
         q.ps_grid = want < cap ? want : cap;
+    }
+    // the forward over those tiles where its A|B image is the multi-slice
+    // kernel's (SH2 = 512)
+    q.fwd_tile = tiles && SH2 == 512;
+    if (tiles && SH2 == 512 && D % 64 == 0) {
+        q.bwd_split = true;
+        q.bwd_rows_kernel = false;
         const int64_t tiles_per_slab = (SH2 / 256) * (2 * D / 128);
         int64_t slabs = 256 / tiles_per_slab;
         if (slabs < 1) slabs = 1;

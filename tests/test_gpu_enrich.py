@@ -23,6 +23,8 @@ CASES = [
     (50, 8, 256, 16, "bf16", -1.0, 16, 0, False),      # h_enriched exactly [B, D]
     (17, 64, 256, 64, "f32", 2.0, 300, 100, False),    # several state slices per workgroup
     (9000, 2, 64, 16, "f32", 0.5, 33, 17, True),       # persistent forward over many groups
+    (8, 256, 512, 128, "f32", -0.5, 640, 512, True),   # the forward over 256-row tiles
+    (12, 64, 512, 64, "bf16", 1.0, 70, 3, False),
 ]
 
 

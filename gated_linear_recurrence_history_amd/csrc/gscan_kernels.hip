@@ -1491,6 +1491,10 @@ __device__ __forceinline__ uint2 wimage_tr(const u4 *Wl, int q, int w, int p, in
     return read_tr(reinterpret_cast<const uint16_t *>(b + 8 * (m & 1)));
 }
 
+// fp32 row pitch of the staging of two 16 x 16 output tiles (32 columns and
+// 16 bytes of padding)
+constexpr int kStgPitch = 36;
+
 // 128-bit stores through a buffer resource of `bytes` bytes at `base`: the
 // hardware drops a store at an offset past the end, so the stores for rows
 // past the batch need no branch, and the compiler's waits on the memory
@@ -1535,9 +1539,10 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     constexpr int kPitch = HC + 8;
     constexpr int kPlanes = LO ? 2 : 1;
     // per-wavefront tile in bf16 elements (DIN: at least the [2][32][16] tile
-    // of the split [dA | dB])
+    // of the split [dA | dB] and the [16][36] fp32 staging of two output tiles)
     constexpr int kTileE = kPlanes * 16 * kPitch;
-    constexpr int kTile = DIN && kTileE < 1024 ? 1024 : kTileE;
+    constexpr int kDinE = 16 * kStgPitch * 2;
+    constexpr int kTile = DIN && kTileE < kDinE ? kDinE : kTileE;
     constexpr int kStage = kWaves2 * kTile * 2;
     constexpr int kRed = 2 * 2 * SH2 * 16 * 4;
     constexpr int kRaw = raw_rows_of(NQ) * 16 * 4;
@@ -1873,7 +1878,13 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             // the group's rows; rows past the batch fall past the resource
             const __amdgpu_buffer_rsrc_t orsc =
                 out_rsrc(dh_out + cur.g * kGroupSamples * K * (int64_t)SH2, (uint32_t)(NR * SH2 * 4));
-            const uint32_t ooff = ((uint32_t)(lr0 + ln) * SH2 + HC * half + 4 * kg) * 4;
+            // Two tiles (32 columns: one 128-byte line of each of the 16 rows)
+            // at a time pass through the tile as [row][column] fp32, so that
+            // each store writes whole lines: lane l takes row l/8 (+ 8),
+            // bytes 16(l % 8) .. +15 of the line.  Half-line stores left
+            // part of the lines to be filled by reads from memory.
+            float *const stg = reinterpret_cast<float *>(tile);
+            const uint32_t ooff = ((uint32_t)(lr0 + (lane >> 3)) * SH2 + HC * half + 4 * (lane & 7)) * 4;
 #pragma unroll
             for (int t = 0; t < NQ; ++t) {
                 const int q = half * NH + t / 2;
@@ -1885,8 +1896,16 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                 f4 o = mfma_bf(wH, dL, zero4());
                 o = mfma_bf(wL, dH, o);
                 o = mfma_bf(wH, dH, o);
-                store_b128(orsc, ooff + 64 * t, o);
-                if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounded read-ahead
+                *reinterpret_cast<f4 *>(stg + ln * kStgPitch + 16 * (t & 1) + 4 * kg) = o;
+                if (t % 2 == 1) {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const f4 v = *reinterpret_cast<const f4 *>(
+                            stg + ((lane >> 3) + 8 * h2) * kStgPitch + 4 * (lane & 7));
+                        store_b128(orsc, ooff + (8 * h2 * SH2 + 32 * (t / 2)) * 4, v);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);  // bounded read-ahead
+                }
             }
         }
 
@@ -1930,7 +1949,9 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                     const Split ds = split8(dv);
                     const __amdgpu_buffer_rsrc_t orsc =
                         out_rsrc(dhs2_out + cur.g * kGroupSamples * (int64_t)SH2, (uint32_t)(nb * SH2 * 4));
-                    const uint32_t ooff = ((uint32_t)ln * SH2 + 32 * wave + 4 * kg) * 4;
+                    // whole-line stores through the staging, as for d_h_history
+                    float *const stg = reinterpret_cast<float *>(tile);
+                    const uint32_t ooff = ((uint32_t)(lane >> 3) * SH2 + 32 * wave + 4 * (lane & 7)) * 4;
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         const uint2 wh0 = wimage_tr(Wl, wave, 2, 0, 16 * t, 8 * (kg & 1), ln);
@@ -1942,7 +1963,13 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                         f4 o = mfma_bf(wH, ds.lo, zero4());
                         o = mfma_bf(wL, ds.hi, o);
                         o = mfma_bf(wH, ds.hi, o);
-                        store_b128(orsc, ooff + 64 * t, o);
+                        *reinterpret_cast<f4 *>(stg + ln * kStgPitch + 16 * t + 4 * kg) = o;
+                    }
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const f4 v = *reinterpret_cast<const f4 *>(
+                            stg + ((lane >> 3) + 8 * h2) * kStgPitch + 4 * (lane & 7));
+                        store_b128(orsc, ooff + 8 * h2 * SH2 * 4, v);
                     }
                 }
             }

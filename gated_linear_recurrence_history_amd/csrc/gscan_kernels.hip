@@ -2654,6 +2654,7 @@ gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
                     float *__restrict__ out)
 {
     extern __shared__ u4 img[];  // [kc][ct][hi, lo][lane]
+    __shared__ float stg[kWaves][16][kStgPitch];  // per-wavefront output staging
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kg = lane >> 4, ln = lane & 15;
     const int nkc = (KD + 31) / 32;
@@ -2702,10 +2703,28 @@ gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
                 acc[ct] = mfma3<true>(w, hs, acc[ct]);
             }
         }
-        if (r < nrows) {
+        if constexpr (CT == 1) {
+            if (r < nrows) *reinterpret_cast<f4 *>(out + r * SH2 + c0 + 4 * kg) = acc[0];
+        } else {
+            // two column tiles (one 128-byte line of each row) at a time
+            // through LDS, so that every store writes whole lines: lane l
+            // takes row l/8 (+ 8), bytes 16(l % 8) .. +15 of the line
+            float *const sg = &stg[wave][0][0];
+            const int64_t r0 = t * kDinRows + 16 * wave + (lane >> 3);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-                *reinterpret_cast<f4 *>(out + r * SH2 + c0 + 16 * ct + 4 * kg) = acc[ct];
+            for (int cp = 0; cp < CT / 2; ++cp) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    *reinterpret_cast<f4 *>(sg + ln * kStgPitch + 16 * u + 4 * kg) = acc[2 * cp + u];
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const f4 v = *reinterpret_cast<const f4 *>(
+                        sg + ((lane >> 3) + 8 * h2) * kStgPitch + 4 * (lane & 7));
+                    const int64_t rr = r0 + 8 * h2;
+                    if (rr < nrows)
+                        *reinterpret_cast<f4 *>(out + rr * SH2 + c0 + 32 * cp + 4 * (lane & 7)) = v;
+                }
+            }
         }
     }
 }

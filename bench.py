@@ -422,7 +422,10 @@ def plan_kernels(w):
     workload `w`: the library's rule, restated for labelling the bench line."""
     slices = w.D // 16
     groups = -(-w.B // 16)
+    perblock = (16 % w.K == 0 or w.K in (32, 64)) and w.SH2 <= 256
     fwd = "gscan_fwd_kernel" if groups <= 512 else "gscan_fwd_persist_kernel"
+    if slices == 1 and perblock and groups > 512:
+        fwd = "gscan_fwd_rows_kernel"
     if slices >= 2 and (w.K >= 16 or groups <= 512):
         if any(slices % sv == 0 and sv * (w.SH2 // 32) <= 32 for sv in (4, 2)):
             fwd = "gscan_fwd_ms_kernel"
@@ -431,7 +434,7 @@ def plan_kernels(w):
         fwd = "gscan_fwd_tile_kernel"
     if tiles and w.SH2 == 512 and w.D % 64 == 0:
         return fwd, ("gscan_bwd_scan_kernel", "gscan_bwd_contract_kernel")
-    if (16 % w.K == 0 or w.K in (32, 64)) and w.SH2 <= 256:
+    if perblock:
         return fwd, ("gscan_bwd_rows_kernel",)
     return fwd, ("gscan_bwd_kernel",)
 

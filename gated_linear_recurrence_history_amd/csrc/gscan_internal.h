@@ -40,6 +40,7 @@ struct Plan {
     // and dL/dC per sample at split_dc (byte offsets)
     bool bwd_split = false;
     bool fwd_tile = false;  // forward over the split backward's tiles (gscan_fwd_tile_kernel)
+    bool fwd_perblock = false;  // forward with the per-block decomposition (gscan_fwd_rows_kernel)
     int64_t split_slabs = 0;
     int64_t ps_grid = 0;
     size_t split_dab = 0, split_dc = 0;

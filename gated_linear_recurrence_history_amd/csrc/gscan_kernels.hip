@@ -1511,16 +1511,22 @@ __device__ __forceinline__ void store_b128(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 // KT: the scan length when fixed at compile time (the index arithmetic and
 // the branches on K then fold), 0 to take it from the argument.
-template <typename TIn, int NQ, int KT, bool DIN>
-__global__ void __launch_bounds__(kThreads2, 1)
-gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
-                      const float *__restrict__ WA, const float *__restrict__ WB,
-                      const float *__restrict__ WC, int64_t B, int Kin, int D, int slices,
-                      int64_t groups, int64_t nrows, float a_shift,
-                      const float *__restrict__ dctx, float *__restrict__ part,
-                      float *__restrict__ dab_out, float *__restrict__ dc_out,
-                      float *__restrict__ dh_out, float *__restrict__ dhs2_out)
+// MODE: kRowsBwd (weight-gradient partials), kRowsBwdDin (and the input
+// gradients) or kRowsFwd (the forward: projection, forward scan, context =
+// C * x_K at each sample's last row; no tile, no reverse walk).
+constexpr int kRowsBwd = 0, kRowsBwdDin = 1, kRowsFwd = 2;
+
+template <typename TIn, int NQ, int KT, int MODE>
+__device__ __forceinline__ void
+rows_pass(const TIn *__restrict__ hh, const TIn *__restrict__ hs2, const float *__restrict__ WA,
+          const float *__restrict__ WB, const float *__restrict__ WC, int64_t B, int Kin, int D,
+          int slices, int64_t groups, int64_t nrows, float a_shift,
+          const float *__restrict__ dctx, float *__restrict__ part, float *__restrict__ dab_out,
+          float *__restrict__ dc_out, float *__restrict__ dh_out, float *__restrict__ dhs2_out,
+          const CtxOut &out)
 {
+    constexpr bool DIN = MODE == kRowsBwdDin;
+    constexpr bool FWD = MODE == kRowsFwd;
     const int K = KT ? KT : Kin;
     constexpr int SH2 = NQ * 32;
     constexpr int NH = NQ / 2;        // units per column half
@@ -1543,13 +1549,13 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     constexpr int kTileE = kPlanes * 16 * kPitch;
     constexpr int kDinE = 16 * kStgPitch * 2;
     constexpr int kTile = DIN && kTileE < kDinE ? kDinE : kTileE;
-    constexpr int kStage = kWaves2 * kTile * 2;
-    constexpr int kRed = 2 * 2 * SH2 * 16 * 4;
+    constexpr int kStage = FWD ? 0 : kWaves2 * kTile * 2;
+    constexpr int kRed = FWD ? 0 : 2 * 2 * SH2 * 16 * 4;
     constexpr int kRaw = raw_rows_of(NQ) * 16 * 4;
     constexpr int kMem = kStage > kRed ? (kStage > kRaw ? kStage : kRaw) : (kRed > kRaw ? kRed : kRaw);
     __shared__ u4 stage_mem[kMem / 16];
     // the current group's h_s2 unit `wave`, split: [wave][plane][sample][column]
-    __shared__ u4 hst_mem[kWaves2 * kPlanes * 16 * 32 * 2 / 16];
+    __shared__ u4 hst_mem[FWD ? 1 : kWaves2 * kPlanes * 16 * 32 * 2 / 16];
 
     int64_t rho;
     int slice;
@@ -1607,10 +1613,12 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         const int nbb = samples_of(gg);
         const int64_t bb = gg * kGroupSamples;
         const TIn *const hsg = hs2 + bb * SH2;
-        const float *const dcg = dctx + bb * D + s0;
         gcv.load(hsg + (uint32_t)((ln < nbb ? ln : nbb - 1) * SH2 + 32 * (wave % NQ)), kg);
-        const int bl = (tid >> 4) & 15, s = tid & 15;
-        gdc = dcg[(uint32_t)((bl < nbb ? bl : nbb - 1) * D + s)];  // masked at use
+        if constexpr (!FWD) {
+            const float *const dcg = dctx + bb * D + s0;
+            const int bl = (tid >> 4) & 15, s = tid & 15;
+            gdc = dcg[(uint32_t)((bl < nbb ? bl : nbb - 1) * D + s)];  // masked at use
+        }
     };
     // C partials and d_context of a group into LDS (weights staged; every
     // reader of the previous group's values is past a barrier)
@@ -1620,14 +1628,16 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         int z;
         asm volatile("s_mov_b32 %0, 0" : "=s"(z));
         const int ltid = tid + z, llane = lane + z;
-        // both halves write the same values; samples past the batch get 0
-        dctl[(ltid >> 4) & 15][ltid & 15] = ((ltid >> 4) & 15) < nbb ? gdc : 0.f;
         // unconditional split and product (see CvLoad::partial); the split
         // unit waits in LDS for this group's dW_C
         const Split hsS = gcv.op(0);
-        uint16_t *const hw = hst + (llane & 15) * 32 + 8 * (llane >> 4);
-        *reinterpret_cast<u4 *>(hw) = hsS.hi;
-        if constexpr (LO) *reinterpret_cast<u4 *>(hw + 16 * 32) = hsS.lo;
+        if constexpr (!FWD) {
+            // both halves write the same values; samples past the batch get 0
+            dctl[(ltid >> 4) & 15][ltid & 15] = ((ltid >> 4) & 15) < nbb ? gdc : 0.f;
+            uint16_t *const hw = hst + (llane & 15) * 32 + 8 * (llane >> 4);
+            *reinterpret_cast<u4 *>(hw) = hsS.hi;
+            if constexpr (LO) *reinterpret_cast<u4 *>(hw + 16 * 32) = hsS.lo;
+        }
         f4 cp = mfma3<LO>(hsS, wop(Wl, wave % NQ, 2, llane), zero4());
         if (wave >= NQ) cp = zero4();
 #pragma unroll
@@ -1675,9 +1685,11 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             }
             const Split sp = pb.op(u);
             pb.load_unit(nrow, kg, u);
-            *reinterpret_cast<u4 *>(tile + ln * kPitch + 32 * u + 8 * kg) = sp.hi;
-            if constexpr (LO)
-                *reinterpret_cast<u4 *>(tile + (16 + ln) * kPitch + 32 * u + 8 * kg) = sp.lo;
+            if constexpr (!FWD) {
+                *reinterpret_cast<u4 *>(tile + ln * kPitch + 32 * u + 8 * kg) = sp.hi;
+                if constexpr (LO)
+                    *reinterpret_cast<u4 *>(tile + (16 + ln) * kPitch + 32 * u + 8 * kg) = sp.lo;
+            }
             pA = mfma3<LO>(sp, wA, pA);
             pB = mfma3<LO>(sp, wB, pB);
             // keep later units' operand reads from being hoisted further
@@ -1718,20 +1730,23 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             for (int w = 0; w < kWaves2; ++w) cs += cvp[w][sj][ln];
             return dcs * cs;
         };
-        float dcv[4], lprev[4] = {0.f, 0.f, 0.f, 0.f};
+        float dcv[4] = {0.f, 0.f, 0.f, 0.f}, lprev[4] = {0.f, 0.f, 0.f, 0.f};
+        float llast = 0.f;
+        if constexpr (!FWD) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int sj = (lr0 + 4 * kg + j) >> kshift;
-            dcv[j] = dctl[sj < 15 ? sj : 15][ln];
-        }
-        const int s3 = (lr0 + 4 * kg + 3) >> kshift;
-        const float llast = lam_k(s3 < 15 ? s3 : 15, dcv[3]);
-        if (K < 4) {
-#pragma unroll
-            for (int j = 1; j < 4; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 const int sj = (lr0 + 4 * kg + j) >> kshift;
-                const int sp = sj - 1 < 0 ? 0 : (sj - 1 < 15 ? sj - 1 : 15);
-                lprev[j] = lam_k(sp, dctl[sp][ln]);
+                dcv[j] = dctl[sj < 15 ? sj : 15][ln];
+            }
+            const int s3 = (lr0 + 4 * kg + 3) >> kshift;
+            llast = lam_k(s3 < 15 ? s3 : 15, dcv[3]);
+            if (K < 4) {
+#pragma unroll
+                for (int j = 1; j < 4; ++j) {
+                    const int sj = (lr0 + 4 * kg + j) >> kshift;
+                    const int sp = sj - 1 < 0 ? 0 : (sj - 1 < 15 ? sj - 1 : 15);
+                    lprev[j] = lam_k(sp, dctl[sp][ln]);
+                }
             }
         }
 
@@ -1812,7 +1827,25 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             const int r = lr0 + 4 * kg + j;
             xbef[j] = tj[j] == 0 ? 0.f : x;
             x = tj[j] == 0 ? beta[j] : gate[j] * x + beta[j];
-            if (half == 0 && r < ce && tj[j] == K - 1) dCl[r >> kshift][ln] = dcv[j] * x;
+            if (half == 0 && r < ce && tj[j] == K - 1) {
+                if constexpr (FWD) {
+                    // context = C * x_K (C from the eight wavefronts' partials)
+                    const int sj = r >> kshift;
+                    float cs = 0.f;
+#pragma unroll
+                    for (int w = 0; w < kWaves2; ++w) cs += cvp[w][sj][ln];
+                    put_context(out, cur.g * kGroupSamples + sj, D, s0 + ln, cs * x);
+                } else {
+                    dCl[r >> kshift][ln] = dcv[j] * x;
+                }
+            }
+        }
+        if constexpr (FWD) {
+            if (c == nch - 1) {
+                __syncthreads();  // every reader of this group's C partials is done
+                if (more) use_group(samples_of(nxt.g));
+            }
+            return;
         }
         // reverse walk: adjoint of each row's output state, entering the
         // lane's last row as lambda_K of its sample times the later gates
@@ -2005,6 +2038,7 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
         step(cur, pA, nxt);
         cur = nxt;
     }
+    if constexpr (FWD) return;
 
     // sums over the four blocks of each half: (b0 + b2) + (b1 + b3), in LDS
     // (over the transposition tiles, once every wavefront is done with its
@@ -2051,6 +2085,37 @@ gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                 accC[t], reinterpret_cast<f4 *>(P + 2 * (int64_t)SH2 * D + ((int64_t)iq * D + s0 + ln) * 4));
         }
     }
+}
+
+template <typename TIn, int NQ, int KT, bool DIN>
+__global__ void __launch_bounds__(kThreads2, 1)
+gscan_bwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
+                      const float *__restrict__ WA, const float *__restrict__ WB,
+                      const float *__restrict__ WC, int64_t B, int Kin, int D, int slices,
+                      int64_t groups, int64_t nrows, float a_shift,
+                      const float *__restrict__ dctx, float *__restrict__ part,
+                      float *__restrict__ dab_out, float *__restrict__ dc_out,
+                      float *__restrict__ dh_out, float *__restrict__ dhs2_out)
+{
+    rows_pass<TIn, NQ, KT, DIN ? kRowsBwdDin : kRowsBwd>(
+        hh, hs2, WA, WB, WC, B, Kin, D, slices, groups, nrows, a_shift, dctx, part, dab_out,
+        dc_out, dh_out, dhs2_out, CtxOut{});
+}
+
+// The forward with the per-block backward's decomposition: one persistent
+// workgroup per CU, the weights staged once, 64-row chunks requested one
+// chunk ahead, each 16-row block projected by two wavefronts (halves of the
+// columns), then the forward scan and the context at each sample's end.
+template <typename TIn, int NQ, int KT>
+__global__ void __launch_bounds__(kThreads2, 1)
+gscan_fwd_rows_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
+                      const float *__restrict__ WA, const float *__restrict__ WB,
+                      const float *__restrict__ WC, int64_t B, int Kin, int D, int slices,
+                      int64_t groups, int64_t nrows, float a_shift, CtxOut out)
+{
+    rows_pass<TIn, NQ, KT, kRowsFwd>(hh, hs2, WA, WB, WC, B, Kin, D, slices, groups, nrows,
+                                     a_shift, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, out);
 }
 
 // ======================== split backward: projection + scans, then contraction
@@ -2735,6 +2800,19 @@ hipError_t fwd_launch(const Plan &p, const void *hh, const void *hs2, const floa
                       const float *WB, const float *WC, float a_shift, const CtxOut &ctx,
                       hipStream_t st)
 {
+    if constexpr (NQ <= 8) {
+        if (p.fwd_perblock) {
+            auto go = [&](auto kern) {
+                hipLaunchKernelGGL(kern, dim3((unsigned)p.bwd_grid), dim3(kThreads2), 0, st,
+                                   static_cast<const TIn *>(hh), static_cast<const TIn *>(hs2), WA,
+                                   WB, WC, p.B, (int)p.K, (int)p.D, p.slices, p.groups,
+                                   p.bwd_rows, a_shift, ctx);
+                return hipGetLastError();
+            };
+            if (p.K == 8) return go(gscan_fwd_rows_kernel<TIn, NQ, 8>);
+            return go(gscan_fwd_rows_kernel<TIn, NQ, 0>);
+        }
+    }
     if (p.fwd_tile) {
         const int64_t ntiles = p.B * p.K / kPsRows;
         auto go = [&](auto kern) {
@@ -2952,6 +3030,10 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
     if (cap < kXcds) cap = kXcds;
     q.bwd_rows = q.fwd_rows < cap ? q.fwd_rows : cap;
     q.bwd_grid = q.bwd_rows * q.slices;
+    // the forward with the same decomposition where one slice holds every
+    // state and each workgroup walks many groups (the one-group-per-workgroup
+    // kernels start faster on a few groups per CU)
+    q.fwd_perblock = q.bwd_rows_kernel && q.slices == 1 && q.groups > kFwdMaxRows;
     const int64_t wsz = SH2 * D;
     q.red_grid = 3 * wsz / kRedCols;
     q.ws_bytes = (size_t)(q.bwd_rows * 3 * wsz * 4);

@@ -85,6 +85,13 @@ SMALL = [
     (20, 64, 512, 192, "f32", 0.25),
     (2000, 64, 512, 64, "f32", 1.0),
     (13, 64, 512, 64, "f32", 0.0),
+    # one state slice and more than 512 groups: the forward with the
+    # per-block decomposition (ragged last group, samples spanning 2 and 4
+    # blocks of a chunk, K = 1 and 16, both input types)
+    (8200, 32, 64, 16, "f32", 0.5),
+    (8250, 64, 64, 16, "f32", -1.0),
+    (8300, 16, 128, 16, "bf16", 2.0),
+    (8195, 1, 64, 16, "f32", 0.0),
 ]
 
 

@@ -7,12 +7,15 @@
 //   C_b[i][j] <- f[i] C_b[i][j] + (1 - f[i]) h_b[i] h_b[j]
 // The page's kernel takes one block per row of C.  Here the update is a
 // pure stream of C (read once, written once) with a small dot product per
-// row in front of it, so one workgroup takes a tile of 4 rows of 8 samples.
-// It requests the gate inputs of the tile (the 8 vectors [h_b ; x_b] and the
-// 4 rows of W_f, 1024 columns per round, L2-resident) and then the tile's
-// first 512 columns of C, stages the gate inputs in LDS, forms the 32 gates
-// (eight lanes per gate, each a strided part of the dot product, added in a
-// fixed tree) while C is in flight, and then updates and stores the tile,
+// row in front of it, so one workgroup takes a tile of 4 rows of 4 samples
+// (small enough that several workgroups per CU, at different phases, keep
+// reads and writes of C in flight together: 8 samples per tile took 15%
+// longer).  It requests the gate inputs of the tile (the 4 vectors
+// [h_b ; x_b] and the 4 rows of W_f, 1024 columns per round, L2-resident)
+// and then the tile's
+// first 512 columns of C, stages the gate inputs in LDS, forms the 16 gates
+// (sixteen lanes per gate, each a strided part of the dot product, added in
+// a fixed tree) while C is in flight, and then updates and stores the tile,
 // 512 columns at a time, with 16-byte accesses.
 // Arithmetic is fp32 throughout; 1 - f is formed as exp(-a) * f for a > 0
 // (no cancellation when the gate saturates).
@@ -25,9 +28,9 @@ namespace {
 
 constexpr int kCifgThreads = 256;
 constexpr int kCifgRows = 4;        // rows of C per tile
-constexpr int kCifgSamples = 8;     // samples per tile
+constexpr int kCifgSamples = 4;     // samples per tile
 constexpr int kCifgPairs = kCifgRows * kCifgSamples;
-constexpr int kCifgLanesPerGate = kCifgThreads / kCifgPairs;  // 8
+constexpr int kCifgLanesPerGate = kCifgThreads / kCifgPairs;  // 16
 constexpr int kCifgCols = 512;      // columns per pass
 constexpr int kCifgPer = kCifgPairs * (kCifgCols / 4) / kCifgThreads;  // 16-byte pieces per thread and pass
 constexpr int kCifgK = 1024;        // gate-input columns staged per round
@@ -42,7 +45,7 @@ gscan_cifg_kernel(float *__restrict__ C, const float *__restrict__ H, const floa
                   const float *__restrict__ W, const float *__restrict__ bias, int64_t B, int d,
                   int din)
 {
-    // gate inputs of one round: [h_b ; x_b] of the tile's 8 samples, then the
+    // gate inputs of one round: [h_b ; x_b] of the tile's samples, then the
     // tile's 4 rows of W_f, each kCifgK columns wide
     __shared__ float stg[kCifgStageRows][kCifgPitch];
     __shared__ float fl[kCifgPairs], fcl[kCifgPairs], hil[kCifgPairs];
@@ -109,9 +112,9 @@ gscan_cifg_kernel(float *__restrict__ C, const float *__restrict__ H, const floa
     f4 cv[kCifgPer];
     load_c(cv, 0);
 
-    // gates: lanes 8p .. 8p+7 form the dot product of W_f row i with
-    // [h_b ; x_b], lane q taking the pieces q, q + 8, ... of each round;
-    // the eight partial sums are added in a fixed tree
+    // gates: lanes 16p .. 16p+15 form the dot product of W_f row i with
+    // [h_b ; x_b], lane q taking the pieces q, q + 16, ... of each round;
+    // the sixteen partial sums are added in a fixed tree
     const int gp = tid / kCifgLanesPerGate, gq = tid % kCifgLanesPerGate;
     const int gs = gp / kCifgRows, gr = kCifgSamples + gp % kCifgRows;
     float acc = 0.f;
@@ -132,9 +135,8 @@ gscan_cifg_kernel(float *__restrict__ C, const float *__restrict__ H, const floa
             acc = fmaf(w[3], c[3], acc);
         }
     }
-    acc += __shfl_xor(acc, 4, kCifgLanesPerGate);
-    acc += __shfl_xor(acc, 2, kCifgLanesPerGate);
-    acc += __shfl_xor(acc, 1, kCifgLanesPerGate);
+#pragma unroll
+    for (int o = kCifgLanesPerGate / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kCifgLanesPerGate);
     if (gq == 0) {
         const bool ok = pair_ok(gp);
         const int64_t b = ok ? b0 + gp / kCifgRows : 0;

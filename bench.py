@@ -29,9 +29,12 @@ Fields beyond the headline value:
   kernels_us        average duration of each kernel: HIP events on the
                     launch stream around a run of back-to-back launches of
                     that kernel alone
-  roofline          the dominant (longest) kernel against HBM bandwidth:
-                    its algorithmic bytes per launch over its average
-                    duration; `traffic` is the HBM bytes per launch that
+  roofline          the dominant (longest) kernel against the roof that
+                    bounds it (the higher of its HBM floor and its MFMA
+                    floor): algorithmic bytes per launch over its average
+                    duration against 8 TB/s, or the bf16 products it issues
+                    (three per fp32 product) against 2.5 PFLOP/s; `traffic`
+                    is the HBM bytes per launch that
                     rocprofv3 counters measured for the same kernel source
                     (profiles/traffic_<kernel>_<workload>.txt), else null;
                     where the backward's phase 1 is the split pair (scan
@@ -41,8 +44,10 @@ Fields beyond the headline value:
                     same workload on this host's cores
   configs           every named workload (tiny, headline, long K, bf16 big
                     batch, wide): forward and backward HIP-event time per call
-                    on resident synthetic inputs, samples/s and the fraction
-                    of 8 TB/s their algorithmic bytes reach
+                    on resident synthetic inputs, samples/s, the fraction
+                    of 8 TB/s their algorithmic bytes reach, and the step's
+                    floor (per pass the higher of its HBM and MFMA times) as
+                    a fraction of its time
   bias_grad_reduce  the batch-parallel bias-gradient reduction on the spec's
                     IQN shape [524288 x 3] (fp32, synthetic N(0, 9)): HIP-event
                     time per call, bytes read against 8 TB/s, and the
@@ -326,10 +331,16 @@ def all_configs(stream):
             times[name] = e0.elapsed_time(e1) * 1e3 / reps
         tot = times["fwd"] + times["bwd"]
         byts = w.fwd_bytes() + w.bwd_bytes()
+        # the step's floor: per pass the higher of its HBM time at 8 TB/s and
+        # its bf16 MFMA time (three products per fp32 product, two for bf16 rows)
+        split = SPLIT_PRODUCTS if w.in_dtype == "f32" else 2
+        floor = sum(max(by / (HBM_PEAK_GBS * 1e9), split * fl / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+                    for by, fl in ((w.fwd_bytes(), w.fwd_flops()), (w.bwd_bytes(), w.bwd_flops())))
         res[w.name] = {"B": w.B, "K": w.K, "SH2": w.SH2, "D": w.D, "in_dtype": w.in_dtype,
                        "fwd_us": round(times["fwd"], 2), "bwd_us": round(times["bwd"], 2),
                        "samples_per_s": round(w.B / (tot * 1e-6), 1),
                        "hbm_frac": round(byts / (tot * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+                       "floor_us": round(floor, 2), "frac_of_floor": round(floor / tot, 4),
                        "reps": reps}
         del t, ctx, dW, ws
         torch.cuda.empty_cache()
@@ -603,16 +614,27 @@ def main():
         bnames = (fname,)
         kname, kus, kbytes, kflops = fname, k_fwd, w.fwd_bytes(), w.fwd_flops()
     t_hbm_us = kbytes / (HBM_PEAK_GBS * 1e9) * 1e6
-    t_mfma_us = SPLIT_PRODUCTS * kflops / (BF16_PEAK_TFLOPS * 1e12) * 1e6
+    # bf16 rows are exact in the high part: two products per fp32 product
+    split = SPLIT_PRODUCTS if w.in_dtype == "f32" else 2
+    t_mfma_us = split * kflops / (BF16_PEAK_TFLOPS * 1e12) * 1e6
     ach = kbytes / (kus * 1e-6) / 1e9
     recs = [traffic_record(k, w.name) for k in bnames]
     traffic = sum(r["traffic_bytes"] for r in recs) if all(recs) else None
-    roof = {"bound": "hbm" if t_hbm_us >= t_mfma_us else "mfma", "achieved": round(ach, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-            "frac_of_read_ceiling": round(ach / rd_gbs, 4),
-            "traffic": traffic,
-            "kernel": kname, "avg_us": round(kus, 3), "algorithmic_bytes": kbytes,
-            "hbm_floor_us": round(t_hbm_us, 3), "mfma_floor_us": round(t_mfma_us, 3)}
+    if t_hbm_us >= t_mfma_us:
+        # bound by HBM: algorithmic bytes over time against 8 TB/s
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "frac_of_read_ceiling": round(ach / rd_gbs, 4)}
+    else:
+        # bound by the matrix cores: the bf16 products the split arithmetic
+        # issues over time against the bf16 peak
+        tflops = split * kflops / (kus * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                "achieved_GBs": round(ach, 1)}
+    roof.update({"traffic": traffic, "kernel": kname, "avg_us": round(kus, 3),
+                 "algorithmic_bytes": kbytes, "algorithmic_flops": kflops,
+                 "hbm_floor_us": round(t_hbm_us, 3), "mfma_floor_us": round(t_mfma_us, 3)})
 
     out = {
         "metric": METRIC,

@@ -2493,29 +2493,29 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
     xraw_t xvs[2][XV];
     f4 yvs[2][YV];
     constexpr int XCOLS = LO ? MT / 4 : MT / 8;   // pieces per X row
+    // a step's rows through buffer resources that end at the slab's last
+    // row: a uniform base, 32-bit lane offsets (the same every step), and
+    // rows past the end read as zeros with no branch
     auto load = [&](int set, int64_t rb) {
+        const int64_t left = r_end - rb;
+        const uint32_t nv = (uint32_t)(left < kCtRows ? (left > 0 ? left : 0) : kCtRows);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<TX *>(X + rb * ldx + m0), (short)0, (int)(nv * ldx * sizeof(TX)), 0x00020000);
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(Y + rb * ldy + n0), (short)0, (int)(nv * ldy * 4), 0x00020000);
 #pragma unroll
         for (int u = 0; u < XV; ++u) {
             const int e = tid + kCtThreads * u;
             const int r = e / XCOLS, c = e % XCOLS;
-            const int64_t gr = rb + r;
-            if (gr < r_end) {
-                if constexpr (LO)
-                    xvs[set][u] = *reinterpret_cast<const f4 *>(X + gr * ldx + m0 + 4 * c);
-                else
-                    xvs[set][u] = *reinterpret_cast<const u4 *>(X + gr * ldx + m0 + 8 * c);
-            } else {
-                if constexpr (LO) xvs[set][u] = zero4();
-                else xvs[set][u] = zero_u4();
-            }
+            const uint32_t off = (uint32_t)(r * ldx + (LO ? 4 : 8) * c) * (uint32_t)sizeof(TX);
+            xvs[set][u] = __builtin_bit_cast(xraw_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
         }
 #pragma unroll
         for (int u = 0; u < YV; ++u) {
             const int e = tid + kCtThreads * u;
             const int r = e / (NT / 4), c = e % (NT / 4);
-            const int64_t gr = rb + r;
-            yvs[set][u] = gr < r_end ? *reinterpret_cast<const f4 *>(Y + gr * ldy + n0 + 4 * c)
-                                     : zero4();
+            const uint32_t off = (uint32_t)(r * ldy + 4 * c) * 4u;
+            yvs[set][u] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(ry, (int)off, 0, 0));
         }
     };
     auto store = [&](int set, int buf) {

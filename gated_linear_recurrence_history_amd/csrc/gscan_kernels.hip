@@ -472,17 +472,16 @@ __device__ __forceinline__ Split wop(const u4 *Wl, int q, int w, int lane)
     return s;
 }
 
-// A|Bv projection of NB 16-row blocks (results in MFMA output layout).
-template <typename TIn, int NQ, int NB>
-__device__ __forceinline__ void project(const PBlk<TIn, NQ> (&blk)[NB], const u4 *Wl, int lane,
-                                        f4 (&aA)[NB], f4 (&aB)[NB])
+// A|Bv projection of one 16-row block (results in MFMA output layout).  The
+// block is taken by reference: a local copy of its registers cost one move
+// per register and block.
+template <typename TIn, int NQ>
+__device__ __forceinline__ void project(const PBlk<TIn, NQ> &blk, const u4 *Wl, int lane,
+                                        f4 &aA, f4 &aB)
 {
     constexpr bool LO = PBlk<TIn, NQ>::kLo;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        aA[b] = zero4();
-        aB[b] = zero4();
-    }
+    aA = zero4();
+    aB = zero4();
     // the weight operands of unit q + 1 are read while unit q is projected
     Split wan = wop(Wl, 0, 0, lane), wbn = wop(Wl, 0, 1, lane);
 #pragma unroll
@@ -492,12 +491,9 @@ __device__ __forceinline__ void project(const PBlk<TIn, NQ> (&blk)[NB], const u4
             wan = wop(Wl, q + 1, 0, lane);
             wbn = wop(Wl, q + 1, 1, lane);
         }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const Split h = blk[b].op(q);
-            aA[b] = mfma3<LO>(h, wa, aA[b]);
-            aB[b] = mfma3<LO>(h, wb, aB[b]);
-        }
+        const Split h = blk.op(q);
+        aA = mfma3<LO>(h, wa, aA);
+        aB = mfma3<LO>(h, wb, aB);
         // keep the weight-operand reads of later units from being hoisted
         // further (they would pin NQ x 16 registers next to the in-flight rows)
         __builtin_amdgcn_sched_barrier(0);
@@ -558,10 +554,7 @@ __device__ __forceinline__ void fwd_block(const PBlk<TIn, NQ> &blk, const u4 *Wl
     const int kg = lane >> 4, ln = lane & 15;
     const RowPos bp = base_pos(base, K);
     f4 aA[1], aB[1];
-    {
-        const PBlk<TIn, NQ> one[1] = {blk};
-        project<TIn, NQ, 1>(one, Wl, lane, aA, aB);
-    }
+    project<TIn, NQ>(blk, Wl, lane, aA[0], aB[0]);
     Aff map[4];
     Aff F = aff_id();
 #pragma unroll
@@ -1164,10 +1157,7 @@ gscan_bwd_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
                     load_t_half<TIn, NQ>(hv0[1], hg, cb, NR, wave, 1, lane);
                 }
             }
-            {
-                const PBlk<TIn, NQ> one[1] = {pb};
-                project<TIn, NQ, 1>(one, Wl, lane, aA, aB);
-            }
+            project<TIn, NQ>(pb, Wl, lane, aA[0], aB[0]);
             if (ab_out) {
                 // the projections A | Bv of this block's rows, for the input
                 // gradients (samples may continue past the chunk, so the

@@ -1598,16 +1598,21 @@ rows_pass(const TIn *__restrict__ hh, const TIn *__restrict__ hs2, const float *
     // can leave the younger ones in flight.
     PBlk<TIn, 1> gcv;
     float gdc = 0.f;
-    auto load_group = [&](int64_t gg) {
+    // need = false (the next chunk continues the current group, so nothing
+    // consumes these registers): every lane reads the group's first line
+    // instead, the same instructions with almost no traffic
+    auto load_group = [&](int64_t gg, bool need = true) {
         // uniform 64-bit bases, 32-bit lane offsets
         const int nbb = samples_of(gg);
         const int64_t bb = gg * kGroupSamples;
         const TIn *const hsg = hs2 + bb * SH2;
-        gcv.load(hsg + (uint32_t)((ln < nbb ? ln : nbb - 1) * SH2 + 32 * (wave % NQ)), kg);
+        const uint32_t ho = (uint32_t)((ln < nbb ? ln : nbb - 1) * SH2 + 32 * (wave % NQ));
+        gcv.load(hsg + (need ? ho : 0u), kg);
         if constexpr (!FWD) {
             const float *const dcg = dctx + bb * D + s0;
             const int bl = (tid >> 4) & 15, s = tid & 15;
-            gdc = dcg[(uint32_t)((bl < nbb ? bl : nbb - 1) * D + s)];  // masked at use
+            const uint32_t dofs = (uint32_t)((bl < nbb ? bl : nbb - 1) * D + s);
+            gdc = dcg[need ? dofs : 0u];  // masked at use
         }
     };
     // C partials and d_context of a group into LDS (weights staged; every
@@ -1646,11 +1651,11 @@ rows_pass(const TIn *__restrict__ hh, const TIn *__restrict__ hs2, const float *
         const int c = cur.c;
         const bool more = nxt.g < groups;
         // the rows of the next chunk's group (consumed at this step's end
-        // when the next chunk starts a group; requested every step, cache
-        // hits otherwise, so that the waits for the older rows of this chunk
-        // stay exact); the next chunk's rows go out right after this chunk's
+        // when the next chunk starts a group; requested every step, one line
+        // otherwise, so that the waits for the older rows of this chunk stay
+        // exact); the next chunk's rows go out right after this chunk's
         // projection, into the registers it frees
-        load_group(more ? nxt.g : cur.g);
+        load_group(more ? nxt.g : cur.g, more && nxt.c == 0);
         // the first unit's weight operands (the rest follow one unit ahead)
         Split wAn = wop(Wl, half * NH, 0, lane), wBn = wop(Wl, half * NH, 1, lane);
         __syncthreads();  // last step's exchange read; this group's C partials visible

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 
-HIP_SOURCES = ["gscan_kernels.hip", "gscan_colsum.hip", "gscan_cifg.hip", "gscan_api.hip"]
+HIP_SOURCES = ["gscan_kernels.hip", "gscan_generic.hip", "gscan_colsum.hip", "gscan_cifg.hip",
+               "gscan_api.hip"]
 
 
 def _hipcc() -> str:

@@ -54,8 +54,8 @@ int check_common(const void *hh, const void *hs2, const float *WA, const float *
         return fail(GSCAN_ERR_INVALID_ARGUMENT, "unknown input dtype %d", dtype);
     if (!gscan::make_plan(B, K, SH2, D, dtype, plan))
         return fail(GSCAN_ERR_UNSUPPORTED_SHAPE,
-                    "unsupported shape B=%lld K=%lld SH2=%lld D=%lld (need 64<=SH2<=512, "
-                    "SH2%%64==0, 16<=D<=256, D%%16==0)",
+                    "unsupported shape B=%lld K=%lld SH2=%lld D=%lld (need 16<=SH2<=1024, "
+                    "SH2%%16==0, 16<=D<=256, D%%16==0)",
                     (long long)B, (long long)K, (long long)SH2, (long long)D);
     if (!aligned16(hh) || !aligned16(hs2) || !aligned16(WA) || !aligned16(WB) || !aligned16(WC))
         return fail(GSCAN_ERR_MISALIGNED, "input pointers must be 16-byte aligned");
@@ -97,7 +97,7 @@ FullLayout full_layout(const gscan::Plan &p)
         f.bytes = p.ws_bytes;
         return f;
     }
-    if (p.bwd_split) {  // the split backward's workspace already holds both
+    if (p.bwd_split || p.generic) {  // the workspace already holds both
         f.dab = p.split_dab;
         f.dc = p.split_dc;
         f.bytes = p.ws_bytes;
@@ -155,6 +155,30 @@ int current_scratch(void **out)
     return GSCAN_OK;
 }
 
+// The forward with the scratch its plan asks for (the materialised
+// projections of the shapes outside the fused kernels), taken from the
+// stream-ordered allocator and released on the same stream.
+int run_forward(const gscan::Plan &plan, const void *hh, const void *hs2, const float *WA,
+                const float *WB, const float *WC, float a_shift, const gscan::CtxOut &out,
+                hipStream_t stream)
+{
+    void *sc = nullptr;
+    if (plan.fwd_scratch) {
+        hipError_t e = hipMallocAsync(&sc, plan.fwd_scratch, stream);
+        if (e != hipSuccess)
+            return fail(GSCAN_ERR_HIP, "forward scratch allocation (%zu bytes) failed: %s",
+                        plan.fwd_scratch, hipGetErrorString(e));
+    }
+    hipError_t e = gscan::launch_forward(plan, hh, hs2, WA, WB, WC, a_shift, out, sc, stream);
+    if (sc) {
+        hipError_t f = hipFreeAsync(sc, stream);
+        if (e == hipSuccess) e = f;
+    }
+    if (e != hipSuccess)
+        return fail(GSCAN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+    return GSCAN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -173,10 +197,8 @@ int gscan_forward_ex(const void *h_history, const void *h_s2, const float *W_A, 
     clear_stale_error();
     gscan::CtxOut out;
     out.ctx = context_out;
-    hipError_t e = gscan::launch_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out,
-                                         stream);
-    if (e != hipSuccess)
-        return fail(GSCAN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+    st = run_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out, stream);
+    if (st != GSCAN_OK) return st;
     g_last_error[0] = '\0';
     return GSCAN_OK;
 }
@@ -216,10 +238,8 @@ int gscan_forward_enrich(const void *h_history, const void *h_s2, const float *W
     out.ctx = context_out;
     out.enr = h_enriched + col_offset;
     out.ld = ld_enriched;
-    hipError_t e = gscan::launch_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out,
-                                         stream);
-    if (e != hipSuccess)
-        return fail(GSCAN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+    st = run_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out, stream);
+    if (st != GSCAN_OK) return st;
     g_last_error[0] = '\0';
     return GSCAN_OK;
 }

@@ -17,7 +17,8 @@ constexpr int kSlice = 16;         // states per workgroup (one MFMA N tile)
 constexpr int kBlockRows = 16;     // h_history rows per wavefront block (MFMA M tile)
 constexpr int kChunkRows = kBlockRows * kWaves;  // rows per backward chunk
 constexpr int kXcds = 8;           // MI355X accelerator complex dies
-constexpr int kMaxSH2 = 512;
+constexpr int kMaxSH2 = 512;       // the fused kernels (SH2 % 64 == 0)
+constexpr int kMaxSH2Generic = 1024;  // the materialised-projection path (SH2 % 16 == 0)
 constexpr int64_t kFwdMaxRows = 512;
 constexpr int kMaxD = 256;
 
@@ -41,12 +42,20 @@ struct Plan {
     bool bwd_split = false;
     bool fwd_tile = false;  // forward over the split backward's tiles (gscan_fwd_tile_kernel)
     bool fwd_perblock = false;  // forward with the per-block decomposition (gscan_fwd_rows_kernel)
+    // shapes outside the fused kernels (SH2 not a multiple of 64, or above
+    // 512): materialised projections, per-(sample, state) scans and plain
+    // contractions into gen_slabs partials.  The workspace holds the
+    // partials, A | Bv per row at split_dab and C per sample at split_dc;
+    // the forward needs fwd_scratch bytes (A | Bv, then C at fwd_cv).
+    bool generic = false;
+    int64_t gen_slabs = 0;
+    size_t fwd_scratch = 0, fwd_cv = 0;
     int64_t split_slabs = 0;
     int64_t ps_grid = 0;
     size_t split_dab = 0, split_dc = 0;
     size_t ws_bytes = 0;    // the backward's workspace (partials, and the split pass's adjoints)
     // phase 1 leaves the final dL/dA | dL/dB and dL/dC (not projections)
-    bool adjoints_final() const { return bwd_rows_kernel || bwd_split; }
+    bool adjoints_final() const { return bwd_rows_kernel || bwd_split || generic; }
     // phase 1 writes the input gradients itself (the per-block kernel with
     // one 16-state slice holds every state of a row)
     bool fused_dinput() const { return bwd_rows_kernel && slices == 1; }
@@ -64,9 +73,21 @@ struct CtxOut {
 // Fills `p` for a validated shape.  Returns false if the shape is unsupported.
 bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p);
 
+// scratch: p.fwd_scratch bytes of device memory (null when that is 0)
 hipError_t launch_forward(const Plan &p, const void *h_history, const void *h_s2,
                           const float *W_A, const float *W_B, const float *W_C,
-                          float a_shift, const CtxOut &out, hipStream_t stream);
+                          float a_shift, const CtxOut &out, void *scratch, hipStream_t stream);
+
+// The materialised-projection path (p.generic): forward into `out` with
+// A | Bv in ab [B*K][2D] and C in cv [B][D] as scratch; phase 1 of the
+// backward into `part` with the adjoints left final in ab and cv.
+hipError_t launch_gen_forward(const Plan &p, const void *hh, const void *hs2, const float *WA,
+                              const float *WB, const float *WC, float a_shift, const CtxOut &ctx,
+                              float *ab, float *cv, hipStream_t st);
+hipError_t launch_gen_partials(const Plan &p, const void *hh, const void *hs2, const float *WA,
+                               const float *WB, const float *WC, float a_shift,
+                               const float *dctx, float *part, float *ab, float *cv,
+                               hipStream_t st);
 
 // Phase 1: per-workgroup weight-gradient partials into `partials`.  When
 // `dab` / `dc` are not null they receive, for the input gradients, either

@@ -2985,7 +2985,7 @@ hipError_t bwd_by_nq(const Plan &p, const void *hh, const void *hs2, const float
 
 bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
 {
-    if (B < 1 || K < 1 || SH2 < 64 || SH2 > kMaxSH2 || SH2 % 64 != 0 || D < kSlice ||
+    if (B < 1 || K < 1 || SH2 < 16 || SH2 > kMaxSH2Generic || SH2 % 16 != 0 || D < kSlice ||
         D > kMaxD || D % kSlice != 0 || (dtype != 0 && dtype != 1))
         return false;
     // 32-bit element offsets inside a 16-sample group (16 * K * SH2 < 2^31)
@@ -2997,6 +2997,32 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
     q.SH2 = SH2;
     q.D = D;
     q.dtype = dtype;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    if (SH2 % 64 != 0 || SH2 > kMaxSH2) {
+        // materialised projections: partial slabs enough for about 1024
+        // contraction workgroups (64 x 64 output tiles), at least 16 rows each
+        q.generic = true;
+        q.slices = (int)(D / kSlice);
+        const int64_t tiles = (SH2 + 63) / 64 * ((2 * D + 63) / 64);
+        const int64_t rows = B * K;
+        int64_t slabs = 1024 / tiles;
+        const int64_t most = (rows + 15) / 16;
+        if (slabs > most) slabs = most;
+        if (slabs < 1) slabs = 1;
+        q.gen_slabs = slabs;
+        q.bwd_rows = slabs;
+        const int64_t wsz = SH2 * D;
+        q.red_grid = 3 * wsz / kRedCols;
+        const size_t part = (size_t)(slabs * 3 * wsz * 4);
+        const size_t abb = (size_t)rows * (size_t)(2 * D) * sizeof(float);
+        q.split_dab = up(part);
+        q.split_dc = up(q.split_dab + abb);
+        q.ws_bytes = q.split_dc + (size_t)(B * D) * sizeof(float);
+        q.fwd_cv = up(abb);
+        q.fwd_scratch = q.fwd_cv + (size_t)(B * D) * sizeof(float);
+        *p = q;
+        return true;
+    }
     q.nq = (int)(SH2 / 32);
     q.slices = (int)(D / kSlice);
     q.groups = (B + kGroupSamples - 1) / kGroupSamples;
@@ -3055,7 +3081,6 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
         int64_t slabs = 256 / tiles_per_slab;
         if (slabs < 1) slabs = 1;
         q.split_slabs = slabs;
-        auto up = [](size_t x) { return (x + 255) / 256 * 256; };
         const size_t part = (size_t)(slabs * 3 * wsz * 4);
         q.split_dab = up(part);
         q.split_dc = up(q.split_dab + (size_t)(B * K) * (size_t)(2 * D) * sizeof(float));
@@ -3069,8 +3094,15 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
 
 hipError_t launch_forward(const Plan &p, const void *hh, const void *hs2, const float *WA,
                           const float *WB, const float *WC, float a_shift, const CtxOut &ctx,
-                          hipStream_t st)
+                          void *scratch, hipStream_t st)
 {
+    if (p.generic) {
+        if (!scratch) return hipErrorInvalidValue;
+        char *sc = static_cast<char *>(scratch);
+        return launch_gen_forward(p, hh, hs2, WA, WB, WC, a_shift, ctx,
+                                  reinterpret_cast<float *>(sc),
+                                  reinterpret_cast<float *>(sc + p.fwd_cv), st);
+    }
     if (p.dtype == 1) return fwd_by_nq<uint16_t>(p, hh, hs2, WA, WB, WC, a_shift, ctx, st);
     return fwd_by_nq<float>(p, hh, hs2, WA, WB, WC, a_shift, ctx, st);
 }
@@ -3080,6 +3112,13 @@ hipError_t launch_backward_partials(const Plan &p, const void *hh, const void *h
                                     float a_shift, const float *dctx, float *part, float *dab,
                                     float *dc, float *dh, float *dhs2, hipStream_t st)
 {
+    if (p.generic) {
+        if (dh) return hipErrorInvalidValue;
+        char *ws = reinterpret_cast<char *>(part);
+        float *ab = dab ? dab : reinterpret_cast<float *>(ws + p.split_dab);
+        float *cv = dc ? dc : reinterpret_cast<float *>(ws + p.split_dc);
+        return launch_gen_partials(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, ab, cv, st);
+    }
     return p.dtype == 1
                ? bwd_by_nq<uint16_t>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, dh, dhs2, st)
                : bwd_by_nq<float>(p, hh, hs2, WA, WB, WC, a_shift, dctx, part, dab, dc, dh, dhs2, st);

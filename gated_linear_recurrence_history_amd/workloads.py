@@ -90,6 +90,14 @@ WORKLOADS = [
 BY_NAME = {w.name: w for w in WORKLOADS}
 HEADLINE = BY_NAME["prod_fp32"]
 
+# The headline shape at hidden widths outside the fused kernels (SH2 not a
+# multiple of 64, and above 512): timed to show what the materialised-
+# projection path costs next to the fused one at SH2 = 256.
+OUT_OF_ENVELOPE = [
+    Workload("prod_sh2_240", 8192, 8, 240, 16, seed=SEED_BASE + 5),
+    Workload("prod_sh2_1024", 8192, 8, 1024, 16, seed=SEED_BASE + 6),
+]
+
 
 # ---- CIFG matrix-memory update (BURT-IMMA CUDA Kernel API Reference,
 # batched_cifg_update, independent mode).  The page quotes batch 32 with

@@ -24,12 +24,21 @@
  * h_history and h_s2 are float32 (GSCAN_F32) or bfloat16 (GSCAN_BF16, raw
  * 16-bit storage).  Everything else is float32; all accumulation is float32.
  *
- * Supported shapes: B >= 1, 1 <= K <= 262144, 64 <= SH2 <= 512 with SH2 % 64 == 0,
- * 16 <= D <= 256 with D % 16 == 0, B*K*SH2 < 2^62.  SH2 stops at 512 because
- * every kernel keeps its weight slice, split into bf16 hi/lo halves, in the
- * 160 KiB of LDS for the whole launch: 192 * SH2 bytes per 16 states (96 KiB
- * at SH2 = 512); SH2 % 64 lets two wavefronts share a row block by halves of
- * 32-column MFMA units.  Other shapes return GSCAN_ERR_UNSUPPORTED_SHAPE.
+ * Supported shapes: B >= 1, 1 <= K <= 262144, 16 <= SH2 <= 1024 with
+ * SH2 % 16 == 0, 16 <= D <= 256 with D % 16 == 0, B*K*SH2 < 2^62; other
+ * shapes return GSCAN_ERR_UNSUPPORTED_SHAPE.  Two paths serve them:
+ *   - SH2 % 64 == 0 and SH2 <= 512: fused kernels that project and scan in
+ *     one pass, keeping their weight slice (split into bf16 hi/lo halves) in
+ *     the 160 KiB of LDS for the whole launch, 192 * SH2 bytes per 16
+ *     states, with two wavefronts sharing a row block by halves of 32-column
+ *     MFMA units;
+ *   - every other supported SH2: the projections of Forward Step 1 are
+ *     written out to device memory (B*K*2D + B*D floats), then scanned and
+ *     contracted by plain fp32 kernels: correct to the same tolerance, at
+ *     several times the fused kernels' cost per byte.  Its forward takes that
+ *     memory from the stream-ordered allocator (hipMallocAsync, released
+ *     with hipFreeAsync on the same stream); its backward keeps it in the
+ *     workspace (the size queries below include it).
  *
  * Pointers: every array pointer is DEVICE memory owned by the caller,
  * 16-byte aligned.  Inputs are read only and must not overlap outputs.  The

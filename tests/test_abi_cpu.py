@@ -58,6 +58,9 @@ def test_workspace_bytes(lib):
     per = 3 * w.SH2 * w.D * 4
     assert n > 0 and n % per == 0 and (n // per) % 8 == 0
     assert lib.gscan_backward_workspace_bytes(w.B, w.K, 100, w.D, 0) == 0
+    assert lib.gscan_backward_workspace_bytes(w.B, w.K, 1040, w.D, 0) == 0
+    assert lib.gscan_backward_workspace_bytes(w.B, w.K, 96, w.D, 0) > 0
+    assert lib.gscan_backward_workspace_bytes(w.B, w.K, 1024, w.D, 0) > 0
     assert lib.gscan_backward_workspace_bytes(w.B, w.K, w.SH2, 24, 0) == 0
     assert lib.gscan_backward_workspace_bytes(w.B, w.K, w.SH2, w.D, 7) == 0
     for cfg in wl.WORKLOADS:
@@ -79,7 +82,8 @@ def _bwd(lib, B=64, K=8, SH2=256, D=16, dctx=FAKE, dwa=FAKE, ws=None, ws_bytes=0
 @pytest.mark.parametrize("kw,code", [
     (dict(hh=None), INVALID), (dict(wc=None), INVALID), (dict(out=None), INVALID),
     (dict(B=0), INVALID), (dict(K=-1), INVALID), (dict(SH2=0), INVALID), (dict(dtype=3), INVALID),
-    (dict(SH2=96), UNSUPPORTED), (dict(SH2=1024), UNSUPPORTED), (dict(D=8), UNSUPPORTED),
+    (dict(SH2=100), UNSUPPORTED), (dict(SH2=8), UNSUPPORTED), (dict(SH2=1040), UNSUPPORTED),
+    (dict(D=8), UNSUPPORTED),
     (dict(D=24), UNSUPPORTED), (dict(D=272), UNSUPPORTED),
     (dict(hh=FAKE + 4), MISALIGNED), (dict(out=FAKE + 8), MISALIGNED),
 ])
@@ -131,6 +135,13 @@ def _split_path(B, K, SH2, D):
     return SH2 == 512 and D % 64 == 0 and K in (64, 256) and B % (256 // K) == 0
 
 
+def _generic_path(B, K, SH2, D):
+    """Shapes outside the fused kernels (SH2 a multiple of 16 that is not a
+    multiple of 64, or above 512): their workspace holds the partials, the
+    projections' adjoints per row and dL/dC per sample."""
+    return SH2 % 64 != 0 or SH2 > 512
+
+
 def _fused_path(B, K, SH2, D):
     """Shapes whose per-block backward writes the input gradients itself (one
     16-state slice; K dividing 16, or 32, 64; SH2 <= 256): no adjoints in the
@@ -141,12 +152,18 @@ def _fused_path(B, K, SH2, D):
 def test_backward_full_workspace_bytes(lib):
     # partials, then dL/dA | dL/dB per row and dL/dC per sample
     shapes = [(c.B, c.K, c.SH2, c.D, 1 if c.in_dtype == "bf16" else 0) for c in wl.WORKLOADS]
-    shapes += [(37, 5, 192, 32, 0), (20, 24, 256, 16, 0), (9, 64, 64, 16, 1), (33, 8, 512, 16, 0)]
+    shapes += [(37, 5, 192, 32, 0), (20, 24, 256, 16, 0), (9, 64, 64, 16, 1), (33, 8, 512, 16, 0),
+               (37, 5, 96, 32, 0), (8, 3, 16, 16, 1), (5, 7, 1024, 256, 0), (300, 9, 784, 48, 1)]
     for B, K, SH2, D, dt in shapes:
         part = lib.gscan_backward_workspace_bytes(B, K, SH2, D, dt)
         full = lib.gscan_backward_full_workspace_bytes(B, K, SH2, D, dt)
         extra = 4 * (B * K * 2 * D + B * D)
-        if _split_path(B, K, SH2, D):
+        if _generic_path(B, K, SH2, D):
+            # slab partials (at least one, at most 1024) then the adjoints
+            per = 3 * SH2 * D * 4
+            assert full == part
+            assert per + extra <= part <= 1024 * per + extra + 512
+        elif _split_path(B, K, SH2, D):
             assert full == part >= extra
         elif _fused_path(B, K, SH2, D):
             assert full == part > 0

@@ -25,6 +25,8 @@ CASES = [
     (9000, 2, 64, 16, "f32", 0.5, 33, 17, True),       # persistent forward over many groups
     (8, 256, 512, 128, "f32", -0.5, 640, 512, True),   # the forward over 256-row tiles
     (12, 64, 512, 64, "bf16", 1.0, 70, 3, False),
+    (41, 6, 112, 32, "f32", 0.5, 45, 13, True),        # materialised-projection forward
+    (7, 3, 640, 16, "bf16", -1.0, 16, 0, False),
 ]
 
 

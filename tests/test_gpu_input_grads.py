@@ -45,6 +45,9 @@ SHAPES = [
     (19, 8, 64, 16, "f32", 3.0),
     (8, 64, 512, 64, "f32", 1.0),     # split backward: adjoints straight from the scan pass
     (2, 256, 512, 128, "bf16", -0.5),
+    (37, 5, 96, 32, "f32", 0.5),      # materialised-projection path: SH2 % 64 != 0
+    (6, 9, 1024, 64, "bf16", -1.0),   # and SH2 above 512
+    (300, 4, 16, 16, "f32", 2.0),
 ]
 
 

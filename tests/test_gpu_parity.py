@@ -92,6 +92,18 @@ SMALL = [
     (8250, 64, 64, 16, "f32", -1.0),
     (8300, 16, 128, 16, "bf16", 2.0),
     (8195, 1, 64, 16, "f32", 0.0),
+    # SH2 a multiple of 16 outside the fused kernels (not a multiple of 64,
+    # or above 512): materialised projections, per-(sample, state) scans,
+    # contractions into row slabs (the smallest and largest SH2, the widest
+    # D, ragged 64-wide tiles, slabs capped by the row count, bf16 rows)
+    (37, 5, 96, 32, "f32", 0.5),
+    (8, 3, 16, 16, "bf16", 0.0),
+    (19, 9, 208, 48, "f32", -1.0),
+    (5, 7, 1024, 256, "f32", 0.25),
+    (11, 17, 768, 64, "bf16", 1.0),
+    (600, 4, 48, 16, "f32", 2.0),
+    (3000, 8, 80, 32, "f32", 0.0),
+    (1, 1, 16, 16, "f32", -3.0),
 ]
 
 
@@ -237,6 +249,7 @@ def test_gate_zero_closed_form_full_batch(name):
     (8192, 8, 256, 16, "f32", 0.0),     # the headline: per-block backward kernel
     (777, 5, 192, 32, "f32", 0.5),      # general backward kernel, ragged batch
     (300, 8, 512, 64, "bf16", -1.0),    # SH2 above the per-block kernel's range
+    (250, 6, 592, 32, "f32", 1.0),      # materialised-projection path
 ], ids=lambda c: "B%d_K%d_S%d_D%d_%s_a%g" % c)
 def test_partials_then_reduce(case):
     """The two exported phases called separately (phase 1 into a caller

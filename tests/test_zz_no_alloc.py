@@ -19,6 +19,7 @@ from tests.gpu_util import DEV, device_inputs, rel_l2, workload  # noqa: E402
 CASES = [
     (8192, 8, 256, 16, "f32", 0.0),    # the headline shape (12 MiB of partials)
     (777, 5, 192, 32, "f32", 0.5),     # smaller, general backward kernel
+    (301, 4, 80, 16, "f32", -1.0),     # materialised-projection path
 ]
 
 

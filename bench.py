@@ -50,8 +50,7 @@ Fields beyond the headline value:
                     a fraction of its time
   out_of_envelope   the headline shape at SH2 = 240 and 1024, outside the
                     fused kernels (the materialised-projection path): the
-                    same figures, the floor taking its fp32 multiply-adds at
-                    the 157.3 TFLOP/s fp32 vector peak
+                    same figures against the same floor
   bias_grad_reduce  the batch-parallel bias-gradient reduction on the spec's
                     IQN shape [524288 x 3] (fp32, synthetic N(0, 9)): HIP-event
                     time per call, bytes read against 8 TB/s, and the
@@ -90,7 +89,6 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 SPLIT_PRODUCTS = 3           # bf16 products per fp32 product
-FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector
 METRIC = "fwd+bwd samples/sec at B=8192,K=8,SH2=256,D=16; % of peak HBM GB/s"
 
 
@@ -295,13 +293,11 @@ def cifg(stream, reps):
     return res
 
 
-def all_configs(stream, workloads=None, fused=True):
+def all_configs(stream, workloads=None):
     """Forward and backward per call on every named workload: one input set
     each, at least 20 calls per figure.  The tiny and headline sets fit in
     the 256 MB Infinity Cache, so their figures here are cache-warm (the
-    headline line above rotates input sets); the larger sets exceed it.
-    fused=False: shapes of the materialised-projection path, whose floor
-    takes its fp32 multiply-adds at the fp32 vector peak."""
+    headline line above rotates input sets); the larger sets exceed it."""
     import numpy as np
     import torch
 
@@ -341,8 +337,7 @@ def all_configs(stream, workloads=None, fused=True):
         # the step's floor: per pass the higher of its HBM time at 8 TB/s and
         # its bf16 MFMA time (three products per fp32 product, two for bf16 rows)
         split = SPLIT_PRODUCTS if w.in_dtype == "f32" else 2
-        fl_s = (split / (BF16_PEAK_TFLOPS * 1e12)) if fused else 1 / (FP32_PEAK_TFLOPS * 1e12)
-        floor = sum(max(by / (HBM_PEAK_GBS * 1e9), fl * fl_s) * 1e6
+        floor = sum(max(by / (HBM_PEAK_GBS * 1e9), split * fl / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
                     for by, fl in ((w.fwd_bytes(), w.fwd_flops()), (w.bwd_bytes(), w.bwd_flops())))
         res[w.name] = {"B": w.B, "K": w.K, "SH2": w.SH2, "D": w.D, "in_dtype": w.in_dtype,
                        "fwd_us": round(times["fwd"], 2), "bwd_us": round(times["bwd"], 2),
@@ -684,7 +679,7 @@ def main():
         out["bias_grad_reduce"] = bias_grad(args, stream, reps)
     if not args.no_configs:
         out["configs"] = all_configs(stream)
-        out["out_of_envelope"] = all_configs(stream, wl.OUT_OF_ENVELOPE, fused=False)
+        out["out_of_envelope"] = all_configs(stream, wl.OUT_OF_ENVELOPE)
     if args.copy_calibration_mib > 0:
         nb = args.copy_calibration_mib << 20
         src = torch.ones(nb, dtype=torch.uint8, device=dev)

@@ -49,6 +49,7 @@ struct Plan {
     // the forward needs fwd_scratch bytes (A | Bv, then C at fwd_cv).
     bool generic = false;
     int64_t gen_slabs = 0;
+    int gen_mt = 0, gen_nt_ab = 0, gen_nt_c = 0;  // contraction tile (h columns, outputs)
     size_t fwd_scratch = 0, fwd_cv = 0;
     int64_t split_slabs = 0;
     int64_t ps_grid = 0;
@@ -88,6 +89,17 @@ hipError_t launch_gen_partials(const Plan &p, const void *hh, const void *hs2, c
                                const float *WB, const float *WC, float a_shift,
                                const float *dctx, float *part, float *ab, float *cv,
                                hipStream_t st);
+
+// out[nrows][NOUT] = in[nrows][KD] x [W1 | W2] (W1 [KD][D1], W2 [KD][NOUT-D1],
+// or W2 null when NOUT == D1); `in` fp32 (dtype 0) or bf16 (dtype 1).
+hipError_t launch_proj(int dtype, const void *in, const float *W1, const float *W2, int64_t D1,
+                       int64_t KD, int64_t NOUT, int64_t nrows, float *out, hipStream_t stream);
+
+// The weight-gradient contractions of the materialised-projection path into
+// p.gen_slabs partials: h_history^T [dA | dB] (ab [B*K][2D]) and h_s2^T dC
+// (cv [B][D]).
+hipError_t launch_gen_contract(const Plan &p, const void *hh, const void *hs2, const float *ab,
+                               const float *cv, float *part, hipStream_t stream);
 
 // Phase 1: per-workgroup weight-gradient partials into `partials`.  When
 // `dab` / `dc` are not null they receive, for the input gradients, either

@@ -2488,16 +2488,20 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
     xraw_t xvs[2][XV];
     f4 yvs[2][YV];
     constexpr int XCOLS = LO ? MT / 4 : MT / 8;   // pieces per X row
-    // a step's rows through buffer resources that end at the slab's last
-    // row: a uniform base, 32-bit lane offsets (the same every step), and
-    // rows past the end read as zeros with no branch
+    // a step's rows through buffer resources that end where the slab's last
+    // row ends: a uniform base, 32-bit lane offsets (the same every step),
+    // and rows past the end read as zeros with no branch.  (A tile that runs
+    // past the row's columns reads the next row's first columns, never past
+    // the slab.)
     auto load = [&](int set, int64_t rb) {
         const int64_t left = r_end - rb;
         const uint32_t nv = (uint32_t)(left < kCtRows ? (left > 0 ? left : 0) : kCtRows);
+        const int xn = nv ? (int)((nv * ldx - m0) * sizeof(TX)) : 0;
+        const int yn = nv ? (int)((nv * ldy - n0) * 4) : 0;
         const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<TX *>(X + rb * ldx + m0), (short)0, (int)(nv * ldx * sizeof(TX)), 0x00020000);
+            const_cast<TX *>(X + rb * ldx + m0), (short)0, xn, 0x00020000);
         const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float *>(Y + rb * ldy + n0), (short)0, (int)(nv * ldy * 4), 0x00020000);
+            const_cast<float *>(Y + rb * ldy + n0), (short)0, yn, 0x00020000);
 #pragma unroll
         for (int u = 0; u < XV; ++u) {
             const int e = tid + kCtThreads * u;
@@ -2591,18 +2595,22 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
             contract(1);
         }
     }
-    // partial of this slab: lane l holds i = m-tile row 4(l/16) + e, o = l % 16
+    // partial of this slab: lane l holds i = m-tile row 4(l/16) + e, o = l % 16.
+    // A tile that runs past SH2 or past the ldy columns of Y (shapes outside
+    // the fused kernels) read neighbouring rows' values or zeros there; those
+    // land only in the entries it does not store.
     float *P = part + slab * 3 * (int64_t)SH2 * D;
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int o = n0 + 16 * (NTW * wn + j) + ln;
+            if (o >= ldy) continue;
             const int which = which0 + o / D, s = o % D;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int ii = m0 + 16 * (MTW * wm + i) + 4 * kg + e;
-                P[((int64_t)which * SH2 + ii) * D + s] = acc[i][j][e];
+                if (ii < SH2) P[((int64_t)which * SH2 + ii) * D + s] = acc[i][j][e];
             }
         }
 }
@@ -2703,32 +2711,56 @@ gscan_adjoint_kernel(float *__restrict__ ab, float *__restrict__ cv,
 // row (one 128-bit store).  Both operands fp32, split hi/lo (3 bf16 MFMA per
 // product).  A workgroup stages the split weights of CT column tiles for all
 // k (zero past KD) in LDS, then walks 64-row tiles (16 rows per wavefront).
+//
+// The same loop serves the projections of Forward Step 1 where they are
+// written out (shapes outside the fused kernels): WT = kWProj reads the
+// weights the other way round, Wk(k, o) = W1[k][o] for o < D1 and
+// W2[k][o - D1] otherwise ([A | Bv] = h_history [W_A | W_B], C = h_s2 W_C),
+// and the rows may be bf16 (exact in the high half: 2 MFMA per product).
 constexpr int kDinRows = 64;
-constexpr int64_t kDinMaxRowBlocks = 1024;  // persistent row blocks per column slice
+constexpr int64_t kDinMaxWorkgroups = 512;  // persistent workgroups over all column slices
+constexpr int kWDin = 0, kWProj = 1;
 
-// WHICH only names the launch in profiles: 0 for d_h_history, 1 for d_h_s2
-template <int CT, int WHICH>
-__global__ void __launch_bounds__(kThreads)
-gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
-                    const float *__restrict__ W2, int D1, int KD, int SH2, int64_t nrows,
-                    float *__restrict__ out)
+template <typename TIn, int CT, int WT>
+__device__ __forceinline__ void
+rows_by_weights(const TIn *__restrict__ in, const float *__restrict__ W1,
+                const float *__restrict__ W2, int D1, int KD, int NOUT, int64_t nrows,
+                float *__restrict__ out)
 {
+    constexpr bool LO = !std::is_same<TIn, uint16_t>::value;
     extern __shared__ u4 img[];  // [kc][ct][hi, lo][lane]
     __shared__ float stg[kWaves][16][kStgPitch];  // per-wavefront output staging
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kg = lane >> 4, ln = lane & 15;
     const int nkc = (KD + 31) / 32;
-    const int c0 = blockIdx.y * CT * 16;
+    // 1-D persistent grid of (row tile, column slice) pairs, XCD-aware: the
+    // slices of one row tile run on one XCD at about the same time, so the
+    // tile comes from HBM once and from that XCD's L2 for the other slices
+    const int nsl = NOUT / (16 * CT);
+    int64_t t0;
+    int slice;
+    decode_block(nsl, t0, slice);
+    const int64_t tstride = (int64_t)gridDim.x / nsl;
+    const int c0 = slice * CT * 16;
     for (int e0 = tid; e0 < nkc * CT * kWave; e0 += kThreads) {
         const int l = e0 & (kWave - 1), ct = (e0 / kWave) % CT, kc = e0 / kWave / CT;
         const int i = c0 + 16 * ct + (l & 15);
         const int k = 32 * kc + 8 * (l >> 4);  // eight k on one side of D1 (D1 % 16 == 0)
         float v[8];
         if (k < KD) {
-            const float *src = k < D1 ? W1 + (int64_t)i * D1 + k
-                                      : W2 + (int64_t)i * (KD - D1) + (k - D1);
+            if constexpr (WT == kWDin) {
+                const float *src = k < D1 ? W1 + (int64_t)i * D1 + k
+                                          : W2 + (int64_t)i * (KD - D1) + (k - D1);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = src[e];
+                for (int e = 0; e < 8; ++e) v[e] = src[e];
+            } else {
+                // eight k of one output column; KD % 16 == 0 keeps them < KD
+                const float *src = i < D1 ? W1 + (int64_t)k * D1 + i
+                                          : W2 + (int64_t)k * (NOUT - D1) + (i - D1);
+                const int pitch = i < D1 ? D1 : NOUT - D1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = src[(int64_t)e * pitch];
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = 0.f;
@@ -2739,32 +2771,75 @@ gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
     }
     __syncthreads();
     const int64_t tiles = (nrows + kDinRows - 1) / kDinRows;
-    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    // the row's k chunks in groups of kG, the next group's loads issued
+    // before the current group's products
+    constexpr int kG = 4;
+    typedef typename std::conditional<LO, f4, u4>::type raw_t;
+    constexpr int kPieces = LO ? 2 : 1;  // 16-byte pieces per chunk and lane
+    const int ngr = (nkc + kG - 1) / kG;
+    // the lane's row in tile t (clamped to the last row)
+    auto row_of = [&](int64_t t) {
         const int64_t r = t * kDinRows + 16 * wave + ln;
-        const float *rowp = in + (r < nrows ? r : nrows - 1) * (int64_t)KD;
+        return in + (r < nrows ? r : nrows - 1) * (int64_t)KD;
+    };
+    auto load_group = [&](raw_t (&v)[kG][kPieces], const TIn *rowp, int g) {
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            const int k = 32 * (g * kG + u) + 8 * kg;
+            const TIn *src = rowp + (k < KD ? k : 0);
+#pragma unroll
+            for (int h = 0; h < kPieces; ++h)
+                v[u][h] = *reinterpret_cast<const raw_t *>(src + h * (16 / sizeof(TIn)));
+        }
+    };
+    raw_t cur[kG][kPieces], nxt[kG][kPieces];
+    if (t0 < tiles) load_group(cur, row_of(t0), 0);
+    for (int64_t t = t0; t < tiles; t += tstride) {
+        const int64_t r = t * kDinRows + 16 * wave + ln;
+        const TIn *rowp = row_of(t);
         f4 acc[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc[ct] = zero4();
-        for (int kc = 0; kc < nkc; ++kc) {
-            const int k = 32 * kc + 8 * kg;
-            const bool kin = k < KD;
-            const float *src = rowp + (kin ? k : 0);
-            const f4 a = *reinterpret_cast<const f4 *>(src);
-            const f4 b = *reinterpret_cast<const f4 *>(src + 4);
-            float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        for (int g = 0; g < ngr; ++g) {
+            // the next group of this tile, or the first of the next tile
+            if (g + 1 < ngr) load_group(nxt, rowp, g + 1);
+            else if (t + tstride < tiles) load_group(nxt, row_of(t + tstride), 0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = kin ? x[e] : 0.f;
-            const Split hs = split8(x);
+            for (int u = 0; u < kG; ++u) {
+                const int kc = g * kG + u;
+                if (kc >= nkc) break;
+                const bool kin = 32 * kc + 8 * kg < KD;
+                Split hs;
+                if constexpr (LO) {
+                    const f4 a = cur[u][0], b = cur[u][kPieces - 1];
+                    float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                Split w;
-                w.hi = img[((kc * CT + ct) * 2 + 0) * kWave + lane];
-                w.lo = img[((kc * CT + ct) * 2 + 1) * kWave + lane];
-                acc[ct] = mfma3<true>(w, hs, acc[ct]);
+                    for (int e = 0; e < 8; ++e) x[e] = kin ? x[e] : 0.f;
+                    hs = split8(x);
+                } else {
+                    hs.hi = kin ? cur[u][0] : zero_u4();
+                    hs.lo = zero_u4();
+                }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    Split w;
+                    w.hi = img[((kc * CT + ct) * 2 + 0) * kWave + lane];
+                    w.lo = img[((kc * CT + ct) * 2 + 1) * kWave + lane];
+                    if constexpr (LO) {
+                        acc[ct] = mfma3<true>(w, hs, acc[ct]);
+                    } else {
+                        acc[ct] = mfma_bf(w.lo, hs.hi, acc[ct]);
+                        acc[ct] = mfma_bf(w.hi, hs.hi, acc[ct]);
+                    }
+                }
             }
+#pragma unroll
+            for (int u = 0; u < kG; ++u)
+#pragma unroll
+                for (int h = 0; h < kPieces; ++h) cur[u][h] = nxt[u][h];
         }
         if constexpr (CT == 1) {
-            if (r < nrows) *reinterpret_cast<f4 *>(out + r * SH2 + c0 + 4 * kg) = acc[0];
+            if (r < nrows) *reinterpret_cast<f4 *>(out + r * NOUT + c0 + 4 * kg) = acc[0];
         } else {
             // two column tiles (one 128-byte line of each row) at a time
             // through LDS, so that every store writes whole lines: lane l
@@ -2782,11 +2857,31 @@ gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
                         sg + ((lane >> 3) + 8 * h2) * kStgPitch + 4 * (lane & 7));
                     const int64_t rr = r0 + 8 * h2;
                     if (rr < nrows)
-                        *reinterpret_cast<f4 *>(out + rr * SH2 + c0 + 32 * cp + 4 * (lane & 7)) = v;
+                        *reinterpret_cast<f4 *>(out + rr * NOUT + c0 + 32 * cp + 4 * (lane & 7)) = v;
                 }
             }
         }
     }
+}
+
+// WHICH only names the launch in profiles: 0 for d_h_history, 1 for d_h_s2
+template <int CT, int WHICH>
+__global__ void __launch_bounds__(kThreads)
+gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
+                    const float *__restrict__ W2, int D1, int KD, int SH2, int64_t nrows,
+                    float *__restrict__ out)
+{
+    rows_by_weights<float, CT, kWDin>(in, W1, W2, D1, KD, SH2, nrows, out);
+}
+
+// WHICH: 0 for [A | Bv] from h_history, 1 for C from h_s2 (profile names)
+template <typename TIn, int CT, int WHICH>
+__global__ void __launch_bounds__(kThreads)
+gscan_proj_kernel(const TIn *__restrict__ in, const float *__restrict__ W1,
+                  const float *__restrict__ W2, int D1, int KD, int NOUT, int64_t nrows,
+                  float *__restrict__ out)
+{
+    rows_by_weights<TIn, CT, kWProj>(in, W1, W2, D1, KD, NOUT, nrows, out);
 }
 
 // ----------------------------------------------------------------- dispatch
@@ -3003,10 +3098,17 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
         // contraction workgroups (64 x 64 output tiles), at least 16 rows each
         q.generic = true;
         q.slices = (int)(D / kSlice);
-        const int64_t tiles = (SH2 + 63) / 64 * ((2 * D + 63) / 64);
+        // contraction tiles: 128 or 256 columns of h, 64 or 128 outputs,
+        // whichever wastes less of the last tile; slabs for about 256
+        // workgroups of the [dA | dB] contraction, at least 32 rows each
+        auto pick = [](int64_t n, int64_t a, int64_t b) { return (n + a - 1) / a * a < (n + b - 1) / b * b ? a : b; };
+        q.gen_mt = (int)pick(SH2, 128, 256);
+        q.gen_nt_ab = (int)pick(2 * D, 64, 128);
+        q.gen_nt_c = (int)pick(D, 64, 128);
+        const int64_t tiles = (SH2 + q.gen_mt - 1) / q.gen_mt * ((2 * D + q.gen_nt_ab - 1) / q.gen_nt_ab);
         const int64_t rows = B * K;
-        int64_t slabs = 1024 / tiles;
-        const int64_t most = (rows + 15) / 16;
+        int64_t slabs = 256 / tiles;
+        const int64_t most = (rows + 31) / 32;
         if (slabs > most) slabs = most;
         if (slabs < 1) slabs = 1;
         q.gen_slabs = slabs;
@@ -3133,24 +3235,48 @@ hipError_t launch_adjoint(const Plan &p, float *ab, float *cv, const float *dctx
     return hipGetLastError();
 }
 
+// Launch shape of rows_by_weights: the widest column slice (CT tiles of 16)
+// whose weight image fits (<= 64 KiB), narrowed while there are too few
+// (row tile, slice) pairs to fill the chip.
+struct RbwShape {
+    int ct;
+    size_t shmem;
+    dim3 grid;
+};
+
+RbwShape rbw_shape(int64_t KD, int64_t NOUT, int64_t nrows)
+{
+    const int nkc = (int)((KD + 31) / 32);
+    const int tiles16 = (int)(NOUT / 16);
+    const int64_t row_tiles = (nrows + kDinRows - 1) / kDinRows;
+    int ct = 16;
+    while (ct > 1 && (ct * nkc > 32 || tiles16 % ct != 0 || row_tiles * (tiles16 / ct) < kDinMaxWorkgroups))
+        ct /= 2;
+    RbwShape r;
+    r.ct = ct;
+    r.shmem = (size_t)nkc * ct * 2 * kWave * sizeof(u4);
+    // persistent row-tile slots per slice, a multiple of the XCD count:
+    // about 512 workgroups in all (two per CU), so that each stages its
+    // weight image once for several row tiles
+    const int nsl = tiles16 / ct;
+    int64_t slots = kDinMaxWorkgroups / nsl / kXcds * kXcds;
+    if (slots < kXcds) slots = kXcds;
+    const int64_t need = (row_tiles + kXcds - 1) / kXcds * kXcds;
+    if (slots > need) slots = need;
+    r.grid = dim3((unsigned)(slots * nsl));
+    return r;
+}
+
 template <int WHICH>
 hipError_t launch_dinput_which(const float *in, const float *W1, const float *W2, int64_t D1,
                                int64_t KD, int64_t SH2, int64_t nrows, float *out, hipStream_t st)
 {
     if (nrows <= 0) return hipSuccess;
-    const int nkc = (int)((KD + 31) / 32);
-    const int tiles16 = (int)(SH2 / 16);
-    const int64_t row_tiles = (nrows + kDinRows - 1) / kDinRows;
-    // widest column slice whose weight image fits (<= 64 KiB), narrowed
-    // while there are too few (row tile, slice) pairs to fill the chip
-    int ct = 16;
-    while (ct > 1 && (ct * nkc > 32 || tiles16 % ct != 0 || row_tiles * (tiles16 / ct) < 1024))
-        ct /= 2;
-    const size_t shmem = (size_t)nkc * ct * 2 * kWave * sizeof(u4);
-    const unsigned gx = (unsigned)(row_tiles < kDinMaxRowBlocks ? row_tiles : kDinMaxRowBlocks);
-    const dim3 grid(gx, (unsigned)(tiles16 / ct));
+    const RbwShape sh = rbw_shape(KD, SH2, nrows);
+    const dim3 grid = sh.grid;
+    const size_t shmem = sh.shmem;
     const int d1 = (int)D1, kd = (int)KD, sh2 = (int)SH2;
-    switch (ct) {
+    switch (sh.ct) {
     case 16: hipLaunchKernelGGL((gscan_dinput_kernel<16, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
     case 8: hipLaunchKernelGGL((gscan_dinput_kernel<8, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
     case 4: hipLaunchKernelGGL((gscan_dinput_kernel<4, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
@@ -3158,6 +3284,82 @@ hipError_t launch_dinput_which(const float *in, const float *W1, const float *W2
     default: hipLaunchKernelGGL((gscan_dinput_kernel<1, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, sh2, nrows, out); break;
     }
     return hipGetLastError();
+}
+
+template <typename TIn, int WHICH>
+hipError_t launch_proj_which(const TIn *in, const float *W1, const float *W2, int64_t D1,
+                             int64_t KD, int64_t NOUT, int64_t nrows, float *out, hipStream_t st)
+{
+    if (nrows <= 0) return hipSuccess;
+    const RbwShape sh = rbw_shape(KD, NOUT, nrows);
+    const dim3 grid = sh.grid;
+    const size_t shmem = sh.shmem;
+    const int d1 = (int)D1, kd = (int)KD, no = (int)NOUT;
+    switch (sh.ct) {
+    case 16: hipLaunchKernelGGL((gscan_proj_kernel<TIn, 16, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, no, nrows, out); break;
+    case 8: hipLaunchKernelGGL((gscan_proj_kernel<TIn, 8, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, no, nrows, out); break;
+    case 4: hipLaunchKernelGGL((gscan_proj_kernel<TIn, 4, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, no, nrows, out); break;
+    case 2: hipLaunchKernelGGL((gscan_proj_kernel<TIn, 2, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, no, nrows, out); break;
+    default: hipLaunchKernelGGL((gscan_proj_kernel<TIn, 1, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, no, nrows, out); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_proj(int dtype, const void *in, const float *W1, const float *W2, int64_t D1,
+                       int64_t KD, int64_t NOUT, int64_t nrows, float *out, hipStream_t st)
+{
+    const bool ab = W2 != nullptr;
+    if (dtype == 1)
+        return ab ? launch_proj_which<uint16_t, 0>(static_cast<const uint16_t *>(in), W1, W2, D1, KD, NOUT, nrows, out, st)
+                  : launch_proj_which<uint16_t, 1>(static_cast<const uint16_t *>(in), W1, W2, D1, KD, NOUT, nrows, out, st);
+    return ab ? launch_proj_which<float, 0>(static_cast<const float *>(in), W1, W2, D1, KD, NOUT, nrows, out, st)
+              : launch_proj_which<float, 1>(static_cast<const float *>(in), W1, W2, D1, KD, NOUT, nrows, out, st);
+}
+
+namespace {
+template <typename TX, int MT, int NT, int WHICH0>
+hipError_t contract_tiles(const Plan &p, const TX *X, const float *Y, int ldy, int64_t rows,
+                          int64_t rps, float *part, hipStream_t st)
+{
+    const dim3 grid((unsigned)p.gen_slabs, (unsigned)((p.SH2 + MT - 1) / MT),
+                    (unsigned)((ldy + NT - 1) / NT));
+    hipLaunchKernelGGL((gscan_bwd_contract_kernel<TX, MT, NT, 4, WHICH0>), grid,
+                       dim3(kCtThreads), 0, st, X, (int)p.SH2, Y, ldy, rows, rps, (int)p.D,
+                       (int)p.SH2, part);
+    return hipGetLastError();
+}
+
+template <typename TX, int WHICH0>
+hipError_t contract_any(const Plan &p, const TX *X, const float *Y, int ldy, int64_t rows,
+                        int64_t rps, float *part, hipStream_t st)
+{
+    const bool m256 = p.gen_mt == 256, n128 = (WHICH0 == 0 ? p.gen_nt_ab : p.gen_nt_c) == 128;
+    if (m256 && n128) return contract_tiles<TX, 256, 128, WHICH0>(p, X, Y, ldy, rows, rps, part, st);
+    if (m256) return contract_tiles<TX, 256, 64, WHICH0>(p, X, Y, ldy, rows, rps, part, st);
+    if (n128) return contract_tiles<TX, 128, 128, WHICH0>(p, X, Y, ldy, rows, rps, part, st);
+    return contract_tiles<TX, 128, 64, WHICH0>(p, X, Y, ldy, rows, rps, part, st);
+}
+}  // namespace
+
+hipError_t launch_gen_contract(const Plan &p, const void *hh, const void *hs2, const float *ab,
+                               const float *cv, float *part, hipStream_t st)
+{
+    const int64_t rows = p.B * p.K;
+    // slabs of whole 32-row steps over the rows; the samples split evenly
+    const int64_t rps = ((rows + p.gen_slabs - 1) / p.gen_slabs + kCtRows - 1) / kCtRows * kCtRows;
+    const int64_t rpsc = (p.B + p.gen_slabs - 1) / p.gen_slabs;
+    const int d2 = (int)(2 * p.D), d = (int)p.D;
+    hipError_t e;
+    if (p.dtype == 1) {
+        e = contract_any<uint16_t, 0>(p, static_cast<const uint16_t *>(hh), ab, d2, rows, rps, part, st);
+        if (e == hipSuccess)
+            e = contract_any<uint16_t, 2>(p, static_cast<const uint16_t *>(hs2), cv, d, p.B, rpsc, part, st);
+    } else {
+        e = contract_any<float, 0>(p, static_cast<const float *>(hh), ab, d2, rows, rps, part, st);
+        if (e == hipSuccess)
+            e = contract_any<float, 2>(p, static_cast<const float *>(hs2), cv, d, p.B, rpsc, part, st);
+    }
+    return e;
 }
 
 hipError_t launch_dinput(const float *in, const float *W1, const float *W2, int64_t D1, int64_t KD,

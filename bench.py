@@ -111,6 +111,9 @@ def parse():
                     help="skip the timing of the bias-gradient reduction")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload forward/backward timings")
+    ap.add_argument("--configs", default="",
+                    help="comma-separated workload names to time in configs / out_of_envelope "
+                         "(default: all of both)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finish with 4 untimed device copies of this many MiB (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -678,8 +681,10 @@ def main():
     if not args.no_bias_grad:
         out["bias_grad_reduce"] = bias_grad(args, stream, reps)
     if not args.no_configs:
-        out["configs"] = all_configs(stream)
-        out["out_of_envelope"] = all_configs(stream, wl.OUT_OF_ENVELOPE)
+        pick = set(args.configs.split(",")) if args.configs else None
+        sel = lambda ws: [c for c in ws if pick is None or c.name in pick]  # noqa: E731
+        out["configs"] = all_configs(stream, sel(wl.WORKLOADS))
+        out["out_of_envelope"] = all_configs(stream, sel(wl.OUT_OF_ENVELOPE))
     if args.copy_calibration_mib > 0:
         nb = args.copy_calibration_mib << 20
         src = torch.ones(nb, dtype=torch.uint8, device=dev)

@@ -194,6 +194,24 @@ def test_parity_full_size(name):
     _euler(x, dW[1], dW[2], ctx.astype(np.float64), tol)
 
 
+@pytest.mark.parametrize("name", [w.name for w in wl.OUT_OF_ENVELOPE])
+def test_parity_out_of_envelope_full_size(name):
+    """The headline shape at hidden widths outside the fused kernels (SH2 =
+    240 and 1024, the materialised-projection path), at the full batch the
+    benchmark times: all of context and all of dW against the oracle."""
+    w = next(c for c in wl.OUT_OF_ENVELOPE if c.name == name)
+    print(f"case full {w.name} B={w.B} K={w.K} SH2={w.SH2} D={w.D} {w.in_dtype}", flush=True)
+    x = synth.make_inputs(w)
+    t = device_inputs(x)
+    ctx = gpu_forward(t, w.K, w.a_shift)
+    dW = gpu_backward(t, w.K, w.a_shift)
+    del t
+    torch.cuda.empty_cache()
+    ref_ctx, ref_dW = _full_reference(w, x)
+    _check(x, w, ctx, dW, ref_ctx, ref_dW, tol=wl.tolerance(w))
+    _euler(x, dW[1], dW[2], ctx.astype(np.float64), wl.tolerance(w))
+
+
 @pytest.mark.parametrize("a_shift", [30.0, -30.0])
 def test_saturated_gates_full_batch(a_shift):
     """Gates saturated at 1 - 1e-13 (+30) or 1e-13 (-30) over the headline

@@ -6,12 +6,12 @@ kernels behind a C ABI, declared in include/gscan.h); `forward` and
 ctypes wrappers over it.  There is no CPU fallback.
 """
 from .binding import (forward, forward_enrich, backward, backward_full,  # noqa: F401
-                      backward_workspace_bytes,
+                      backward_workspace_bytes, forward_workspace_bytes,
                       backward_full_workspace_bytes, backward_partials, backward_reduce,
                       batched_cifg_update, bias_grad_reduce, library_path, GScanError)
 from . import workloads  # noqa: F401
 
 __all__ = ["forward", "forward_enrich", "backward", "backward_full", "backward_workspace_bytes",
-           "backward_full_workspace_bytes", "backward_partials", "backward_reduce",
-           "batched_cifg_update", "bias_grad_reduce", "library_path", "GScanError",
+           "forward_workspace_bytes", "backward_full_workspace_bytes", "backward_partials",
+           "backward_reduce", "batched_cifg_update", "bias_grad_reduce", "library_path", "GScanError",
            "workloads"]

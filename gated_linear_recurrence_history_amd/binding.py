@@ -45,13 +45,13 @@ def lib():
                                      vp]
         L.gscan_backward.restype = ctypes.c_int
         L.gscan_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp,
-                                       ctypes.c_int, f32, vp]
+                                       ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.gscan_forward_ex.restype = ctypes.c_int
         L.gscan_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp,
                                         ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.gscan_backward_ex.restype = ctypes.c_int
         L.gscan_forward_enrich.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, i64,
-                                           i64, ctypes.c_int, f32, vp]
+                                           i64, ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.gscan_forward_enrich.restype = ctypes.c_int
         L.gscan_batched_cifg_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         L.gscan_batched_cifg_update.restype = ctypes.c_int
@@ -76,6 +76,8 @@ def lib():
         L.gscan_bias_grad_reduce_workspace_bytes.restype = ctypes.c_size_t
         L.gscan_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.gscan_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.gscan_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        L.gscan_forward_workspace_bytes.restype = ctypes.c_size_t
         L.gscan_status_string.argtypes = [ctypes.c_int]
         L.gscan_status_string.restype = ctypes.c_char_p
         L.gscan_last_error.argtypes = []
@@ -167,24 +169,50 @@ def _check_workspace(ws, need, dev):
         raise ValueError(f"workspace holds {ws.numel()} bytes, needs {need}")
 
 
+def forward_workspace_bytes(B: int, K: int, SH2: int, D: int, bf16: bool = False) -> int:
+    return int(lib().gscan_forward_workspace_bytes(B, K, SH2, D,
+                                                   GSCAN_BF16 if bf16 else GSCAN_F32))
+
+
+def _forward_workspace(workspace, B, K, SH2, D, code, dev):
+    """(pointer, bytes, tensor to keep alive) of the forward's workspace: the
+    caller's (checked), or one from torch's caching allocator where the shape
+    needs one, or none."""
+    import torch
+    need = int(lib().gscan_forward_workspace_bytes(B, K, SH2, D, code))
+    if workspace is not None:
+        _check_workspace(workspace, need, dev)
+        return workspace.data_ptr(), workspace.numel(), workspace
+    if need == 0:
+        return None, 0, None
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    return ws.data_ptr(), need, ws
+
+
 def forward(h_history, h_s2, W_A, W_B, W_C, K: int, a_shift: float = 0.0, out=None,
-            stream=None):
-    """context[B, D] (float32) = C * x_K for every (sample, state)."""
+            workspace=None, stream=None):
+    """context[B, D] (float32) = C * x_K for every (sample, state).
+
+    `workspace` may be a uint8 device tensor of at least forward_workspace_bytes()
+    bytes (only shapes outside the fused kernels use one); otherwise one is
+    taken from torch's caching allocator where needed.
+    """
     import torch
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
     if out is None:
         out = torch.empty((B, D), dtype=torch.float32, device=dev)
     else:
         _check_f32(out, (B, D), dev, "out")
+    wp, wn, _keep = _forward_workspace(workspace, B, K, SH2, D, code, dev)
     _check(lib().gscan_forward_ex(
         h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
-        W_C.data_ptr(), B, K, SH2, D, out.data_ptr(), code, float(a_shift),
+        W_C.data_ptr(), B, K, SH2, D, out.data_ptr(), code, float(a_shift), wp, wn,
         _stream_handle(stream, dev)))
     return out
 
 
 def forward_enrich(h_history, h_s2, W_A, W_B, W_C, K: int, h_enriched, col_offset: int = 0,
-                   a_shift: float = 0.0, context_out=None, stream=None):
+                   a_shift: float = 0.0, context_out=None, workspace=None, stream=None):
     """Adds context[b, s] into h_enriched[b, col_offset + s] in place
     (h_enriched: contiguous float32 [B, ld] on the inputs' device) and, if
     `context_out` is given ([B, D] float32), writes the context there too.
@@ -200,10 +228,11 @@ def forward_enrich(h_history, h_s2, W_A, W_B, W_C, K: int, h_enriched, col_offse
     if context_out is not None:
         _check_f32(context_out, (B, D), dev, "context_out")
         cptr = context_out.data_ptr()
+    wp, wn, _keep = _forward_workspace(workspace, B, K, SH2, D, code, dev)
     _check(lib().gscan_forward_enrich(
         h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
         W_C.data_ptr(), B, K, SH2, D, cptr, h_enriched.data_ptr(), ld, int(col_offset), code,
-        float(a_shift), _stream_handle(stream, dev)))
+        float(a_shift), wp, wn, _stream_handle(stream, dev)))
     return h_enriched
 
 
@@ -214,10 +243,12 @@ def prepare_forward_enrich(h_history, h_s2, W_A, W_B, W_C, K, h_enriched, col_of
     ld = int(h_enriched.shape[1])
     if not 0 <= int(col_offset) <= ld - D:
         raise ValueError("col_offset out of range")
+    wp, wn, ws = _forward_workspace(None, B, K, SH2, D, code, dev)
     args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
             W_C.data_ptr(), B, K, SH2, D, None, h_enriched.data_ptr(), ld, int(col_offset), code,
-            ctypes.c_float(a_shift), _stream_handle(stream, dev))
-    return Prepared(lib().gscan_forward_enrich, args, (h_history, h_s2, W_A, W_B, W_C, h_enriched))
+            ctypes.c_float(a_shift), wp, wn, _stream_handle(stream, dev))
+    return Prepared(lib().gscan_forward_enrich, args,
+                    (h_history, h_s2, W_A, W_B, W_C, h_enriched, ws))
 
 
 def batched_cifg_update(C_batch, H, X, W_f, b_f, stream=None):
@@ -417,10 +448,11 @@ class Prepared:
 def prepare_forward(h_history, h_s2, W_A, W_B, W_C, K, out, a_shift=0.0, stream=None):
     dev, code, B, K, SH2, D = _prep(h_history, h_s2, W_A, W_B, W_C, K)
     _check_f32(out, (B, D), dev, "out")
+    wp, wn, ws = _forward_workspace(None, B, K, SH2, D, code, dev)
     args = (h_history.data_ptr(), h_s2.data_ptr(), W_A.data_ptr(), W_B.data_ptr(),
-            W_C.data_ptr(), B, K, SH2, D, out.data_ptr(), code, ctypes.c_float(a_shift),
+            W_C.data_ptr(), B, K, SH2, D, out.data_ptr(), code, ctypes.c_float(a_shift), wp, wn,
             _stream_handle(stream, dev))
-    return Prepared(lib().gscan_forward_ex, args, (h_history, h_s2, W_A, W_B, W_C, out))
+    return Prepared(lib().gscan_forward_ex, args, (h_history, h_s2, W_A, W_B, W_C, out, ws))
 
 
 def prepare_backward(h_history, h_s2, W_A, W_B, W_C, K, d_context, out, workspace,

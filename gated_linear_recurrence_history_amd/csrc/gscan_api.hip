@@ -155,13 +155,34 @@ int current_scratch(void **out)
     return GSCAN_OK;
 }
 
+// A caller's forward workspace, checked only where the plan uses one.
+int check_forward_workspace(const void *workspace, size_t workspace_bytes,
+                            const gscan::Plan &plan)
+{
+    if (!plan.fwd_scratch || !workspace) return GSCAN_OK;
+    if (workspace_bytes < plan.fwd_scratch)
+        return fail(GSCAN_ERR_WORKSPACE_TOO_SMALL, "forward workspace %zu bytes < required %zu",
+                    workspace_bytes, plan.fwd_scratch);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(GSCAN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    return GSCAN_OK;
+}
+
 // The forward with the scratch its plan asks for (the materialised
-// projections of the shapes outside the fused kernels), taken from the
-// stream-ordered allocator and released on the same stream.
+// projections of the shapes outside the fused kernels): the caller's
+// workspace, or memory from the stream-ordered allocator released on the
+// same stream.
 int run_forward(const gscan::Plan &plan, const void *hh, const void *hs2, const float *WA,
                 const float *WB, const float *WC, float a_shift, const gscan::CtxOut &out,
-                hipStream_t stream)
+                void *workspace, hipStream_t stream)
 {
+    if (plan.fwd_scratch && workspace) {
+        hipError_t e = gscan::launch_forward(plan, hh, hs2, WA, WB, WC, a_shift, out, workspace,
+                                             stream);
+        if (e != hipSuccess)
+            return fail(GSCAN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+        return GSCAN_OK;
+    }
     void *sc = nullptr;
     if (plan.fwd_scratch) {
         hipError_t e = hipMallocAsync(&sc, plan.fwd_scratch, stream);
@@ -186,7 +207,7 @@ extern "C" {
 int gscan_forward_ex(const void *h_history, const void *h_s2, const float *W_A, const float *W_B,
                      const float *W_C, int64_t B, int64_t K, int64_t SH2, int64_t D,
                      float *context_out, gscan_dtype_t in_dtype, float a_shift,
-                     hipStream_t stream)
+                     void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     gscan::Plan plan;
     int st = check_common(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, (int)in_dtype, &plan);
@@ -194,10 +215,11 @@ int gscan_forward_ex(const void *h_history, const void *h_s2, const float *W_A, 
     if (!context_out) return fail(GSCAN_ERR_INVALID_ARGUMENT, "null context_out");
     if (!aligned16(context_out))
         return fail(GSCAN_ERR_MISALIGNED, "context_out must be 16-byte aligned");
+    if ((st = check_forward_workspace(workspace, workspace_bytes, plan)) != GSCAN_OK) return st;
     clear_stale_error();
     gscan::CtxOut out;
     out.ctx = context_out;
-    st = run_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out, stream);
+    st = run_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out, workspace, stream);
     if (st != GSCAN_OK) return st;
     g_last_error[0] = '\0';
     return GSCAN_OK;
@@ -207,7 +229,7 @@ int gscan_forward_enrich(const void *h_history, const void *h_s2, const float *W
                          const float *W_B, const float *W_C, int64_t B, int64_t K, int64_t SH2,
                          int64_t D, float *context_out, float *h_enriched, int64_t ld_enriched,
                          int64_t col_offset, gscan_dtype_t in_dtype, float a_shift,
-                         hipStream_t stream)
+                         void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     gscan::Plan plan;
     int st = check_common(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, (int)in_dtype, &plan);
@@ -233,12 +255,13 @@ int gscan_forward_enrich(const void *h_history, const void *h_s2, const float *W
         if (c0 < e1 && e0 < c1)
             return fail(GSCAN_ERR_INVALID_ARGUMENT, "context_out overlaps h_enriched");
     }
+    if ((st = check_forward_workspace(workspace, workspace_bytes, plan)) != GSCAN_OK) return st;
     clear_stale_error();
     gscan::CtxOut out;
     out.ctx = context_out;
     out.enr = h_enriched + col_offset;
     out.ld = ld_enriched;
-    st = run_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out, stream);
+    st = run_forward(plan, h_history, h_s2, W_A, W_B, W_C, a_shift, out, workspace, stream);
     if (st != GSCAN_OK) return st;
     g_last_error[0] = '\0';
     return GSCAN_OK;
@@ -249,7 +272,16 @@ int gscan_forward(const void *h_history, const void *h_s2, const float *W_A, con
                   float *context_out, hipStream_t stream)
 {
     return gscan_forward_ex(h_history, h_s2, W_A, W_B, W_C, B, K, SH2, D, context_out, GSCAN_F32,
-                            0.0f, stream);
+                            0.0f, nullptr, 0, stream);
+}
+
+size_t gscan_forward_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
+                                     gscan_dtype_t in_dtype)
+{
+    if (B <= 0 || K <= 0 || SH2 <= 0 || D <= 0) return 0;
+    gscan::Plan plan;
+    if (!gscan::make_plan(B, K, SH2, D, (int)in_dtype, &plan)) return 0;
+    return plan.fwd_scratch;
 }
 
 size_t gscan_backward_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,

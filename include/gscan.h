@@ -33,12 +33,13 @@
  *     states, with two wavefronts sharing a row block by halves of 32-column
  *     MFMA units;
  *   - every other supported SH2: the projections of Forward Step 1 are
- *     written out to device memory (B*K*2D + B*D floats), then scanned and
- *     contracted by plain fp32 kernels: correct to the same tolerance, at
- *     several times the fused kernels' cost per byte.  Its forward takes that
- *     memory from the stream-ordered allocator (hipMallocAsync, released
- *     with hipFreeAsync on the same stream); its backward keeps it in the
- *     workspace (the size queries below include it).
+ *     written out to device memory (B*K*2D + B*D floats), then scanned, and
+ *     the weight gradients contracted from them, by separate kernels (the
+ *     same split products, the same tolerances, about twice the fused
+ *     kernels' time per byte).  Its forward takes that memory from the
+ *     caller's workspace or, without one, from the stream-ordered allocator
+ *     (hipMallocAsync, released with hipFreeAsync on the same stream); its
+ *     backward keeps it in the workspace (the size queries include it).
  *
  * Pointers: every array pointer is DEVICE memory owned by the caller,
  * 16-byte aligned.  Inputs are read only and must not overlap outputs.  The
@@ -85,7 +86,7 @@ enum {
 
 /*
  * Forward pass (Forward Steps 1-2): writes context_out[B][D].
- * Equivalent to gscan_forward_ex(..., GSCAN_F32, 0.0f, stream).
+ * Equivalent to gscan_forward_ex(..., GSCAN_F32, 0.0f, NULL, 0, stream).
  */
 int gscan_forward(const void *h_history, const void *h_s2,
                   const float *W_A, const float *W_B, const float *W_C,
@@ -106,15 +107,15 @@ int gscan_forward(const void *h_history, const void *h_s2,
  * device memory, 4-byte aligned; requires D <= ld_enriched and
  * 0 <= col_offset <= ld_enriched - D (INVALID_ARGUMENT otherwise).  The add
  * is a read-modify-write of h_enriched in stream order: a concurrent writer
- * of the same rows on another stream races.  Other arguments and errors as
- * for gscan_forward_ex.
+ * of the same rows on another stream races.  Other arguments (workspace
+ * included) and errors as for gscan_forward_ex.
  */
 int gscan_forward_enrich(const void *h_history, const void *h_s2,
                          const float *W_A, const float *W_B, const float *W_C,
                          int64_t B, int64_t K, int64_t SH2, int64_t D,
                          float *context_out, float *h_enriched, int64_t ld_enriched,
                          int64_t col_offset, gscan_dtype_t in_dtype, float a_shift,
-                         hipStream_t stream);
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Backward pass (Backward Steps 1-3): writes dW_A, dW_B, dW_C [SH2][D] for
@@ -130,14 +131,26 @@ int gscan_backward(const void *h_history, const void *h_s2,
                    hipStream_t stream);
 
 /*
- * Forward with input dtype and gate bias: a_shift is a constant added to
- * every A value before the sigmoid (it receives no gradient).
+ * Forward with input dtype, gate bias and an optional caller workspace.
+ * a_shift is a constant added to every A value before the sigmoid (it
+ * receives no gradient).  workspace: device memory of at least
+ * gscan_forward_workspace_bytes() bytes, 256-byte aligned, or NULL to let the
+ * call allocate stream-ordered.  Only the shapes outside the fused kernels
+ * use it (for the projections of Forward Step 1); for the others the size
+ * query returns 0 and workspace / workspace_bytes are ignored.  Contents on
+ * entry are ignored.
  */
 int gscan_forward_ex(const void *h_history, const void *h_s2,
                      const float *W_A, const float *W_B, const float *W_C,
                      int64_t B, int64_t K, int64_t SH2, int64_t D,
                      float *context_out, gscan_dtype_t in_dtype, float a_shift,
-                     hipStream_t stream);
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes gscan_forward_ex and gscan_forward_enrich need for this
+ * shape: 0 where none is needed, and 0 for an unsupported shape (the calls
+ * themselves report that). */
+size_t gscan_forward_workspace_bytes(int64_t B, int64_t K, int64_t SH2, int64_t D,
+                                     gscan_dtype_t in_dtype);
 
 /*
  * Backward with input dtype, gate bias and an optional caller workspace.

@@ -52,6 +52,21 @@ def test_status_strings(lib):
     assert lib.gscan_version() >= 100
 
 
+def test_forward_workspace_bytes(lib):
+    # none for the fused kernels' shapes; A | Bv per row and C per sample
+    # (fp32, 256-byte aligned sections) outside them
+    for c in wl.WORKLOADS:
+        assert lib.gscan_forward_workspace_bytes(c.B, c.K, c.SH2, c.D,
+                                                 1 if c.in_dtype == "bf16" else 0) == 0
+    for B, K, SH2, D in [(64, 8, 96, 16), (5, 7, 1024, 256), (1, 1, 16, 16), (300, 9, 784, 48)]:
+        n = lib.gscan_forward_workspace_bytes(B, K, SH2, D, 0)
+        need = 4 * (B * K * 2 * D + B * D)
+        assert need <= n <= need + 256
+    assert lib.gscan_forward_workspace_bytes(64, 8, 100, 16, 0) == 0
+    assert lib.gscan_forward_workspace_bytes(64, 8, 96, 16, 7) == 0
+    assert lib.gscan_forward_workspace_bytes(0, 8, 96, 16, 0) == 0
+
+
 def test_workspace_bytes(lib):
     w = wl.HEADLINE
     n = lib.gscan_backward_workspace_bytes(w.B, w.K, w.SH2, w.D, 0)
@@ -69,8 +84,9 @@ def test_workspace_bytes(lib):
 
 
 def _fwd(lib, hh=FAKE, hs=FAKE, wa=FAKE, wb=FAKE, wc=FAKE, B=64, K=8, SH2=256, D=16, out=FAKE,
-         dtype=0):
-    return lib.gscan_forward_ex(hh, hs, wa, wb, wc, B, K, SH2, D, out, dtype, 0.0, None)
+         dtype=0, ws=None, ws_bytes=0):
+    return lib.gscan_forward_ex(hh, hs, wa, wb, wc, B, K, SH2, D, out, dtype, 0.0, ws, ws_bytes,
+                                None)
 
 
 def _bwd(lib, B=64, K=8, SH2=256, D=16, dctx=FAKE, dwa=FAKE, ws=None, ws_bytes=0, dtype=0,
@@ -86,6 +102,10 @@ def _bwd(lib, B=64, K=8, SH2=256, D=16, dctx=FAKE, dwa=FAKE, ws=None, ws_bytes=0
     (dict(D=8), UNSUPPORTED),
     (dict(D=24), UNSUPPORTED), (dict(D=272), UNSUPPORTED),
     (dict(hh=FAKE + 4), MISALIGNED), (dict(out=FAKE + 8), MISALIGNED),
+    # a caller workspace is checked only where the shape uses one
+    (dict(SH2=96, ws=FAKE, ws_bytes=16), WS_SMALL),
+    (dict(SH2=96, ws=FAKE + 16, ws_bytes=1 << 40), MISALIGNED),
+    (dict(SH2=1024, dtype=1, ws=FAKE, ws_bytes=256), WS_SMALL),
 ])
 def test_forward_validation(lib, kw, code):
     assert _fwd(lib, **kw) == code
@@ -215,7 +235,7 @@ def test_backward_noalloc_limit_message(lib):
 
 def _enrich(lib, B=64, K=8, SH2=256, D=16, ctx=None, he=FAKE, ld=256, off=0, dtype=0, hh=FAKE):
     return lib.gscan_forward_enrich(hh, FAKE, FAKE, FAKE, FAKE, B, K, SH2, D, ctx, he, ld, off,
-                                    dtype, 0.0, None)
+                                    dtype, 0.0, None, 0, None)
 
 
 @pytest.mark.parametrize("kw,code", [

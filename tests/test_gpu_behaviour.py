@@ -28,10 +28,10 @@ def test_bitwise_reproducible():
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("K", [8, 5, 70])
-def test_non_finite_stays_in_its_sample(K):
-    w = workload(40, K, 128, 32, seed=5)
-    print(f"case nonfinite K={K}", flush=True)
+@pytest.mark.parametrize("K,SH2", [(8, 128), (5, 128), (70, 128), (8, 80), (6, 1008)])
+def test_non_finite_stays_in_its_sample(K, SH2):
+    w = workload(40, K, SH2, 32, seed=5)
+    print(f"case nonfinite K={K} SH2={SH2}", flush=True)
     x = synth.make_inputs(w)
     clean = gpu_forward(device_inputs(x), K, 0.0)
     y = {k: v.copy() for k, v in x.items()}
@@ -85,7 +85,7 @@ def test_errors_leave_outputs_untouched():
         L = binding.lib()
         st = L.gscan_forward_ex(t["h_history"].data_ptr(), t["h_s2"].data_ptr(),
                                 bad_W.data_ptr(), bad_W.data_ptr(), bad_W.data_ptr(), w.B, w.K,
-                                w.SH2, 24, out.data_ptr(), 0, 0.0, None)
+                                w.SH2, 24, out.data_ptr(), 0, 0.0, None, 0, None)
         binding._check(st)
     assert ei.value.status == 2
     torch.cuda.synchronize()
@@ -187,3 +187,40 @@ def test_graph_replays_input_grads_and_bias_grad():
         torch.cuda.synchronize()
         for a, b in zip(got, [r.cpu().numpy() for r in ref] + [refg.cpu().numpy()]):
             assert np.array_equal(a, b), i
+
+
+def test_forward_caller_workspace():
+    """A shape outside the fused kernels: the forward with a caller's
+    workspace gives bitwise the result of the call's own stream-ordered
+    allocation, for the plain and the enrich entry points; a workspace that
+    is too small is refused before anything runs."""
+    w = workload(333, 6, 208, 32, seed=13)
+    print("case forward workspace", flush=True)
+    t = device_inputs(synth.make_inputs(w))
+    L = binding.lib()
+    need = L.gscan_forward_workspace_bytes(w.B, w.K, w.SH2, w.D, 0)
+    assert need >= 4 * (w.B * w.K * 2 * w.D + w.B * w.D)
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    ins = [t[k].data_ptr() for k in ("h_history", "h_s2", "W_A", "W_B", "W_C")]
+    own = torch.full((w.B, w.D), 7.0, device=DEV)
+    mine = torch.full((w.B, w.D), 7.0, device=DEV)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    assert L.gscan_forward_ex(*ins, w.B, w.K, w.SH2, w.D, own.data_ptr(), 0, 0.0, None, 0,
+                              stream) == 0
+    assert L.gscan_forward_ex(*ins, w.B, w.K, w.SH2, w.D, mine.data_ptr(), 0, 0.0,
+                              ws.data_ptr(), need, stream) == 0
+    small = torch.full((w.B, w.D), 7.0, device=DEV)
+    assert L.gscan_forward_ex(*ins, w.B, w.K, w.SH2, w.D, small.data_ptr(), 0, 0.0,
+                              ws.data_ptr(), need - 4, stream) == 4
+    torch.cuda.synchronize()
+    assert torch.equal(own, mine)
+    assert torch.all(small == 7.0)
+    he1 = torch.zeros((w.B, 50), device=DEV)
+    he2 = torch.zeros((w.B, 50), device=DEV)
+    gs.forward_enrich(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K, he1,
+                      col_offset=3)
+    assert L.gscan_forward_enrich(*ins, w.B, w.K, w.SH2, w.D, None, he2.data_ptr(), 50, 3, 0, 0.0,
+                                  ws.data_ptr(), need, stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(he1, he2)
+    assert torch.equal(he1[:, 3:3 + w.D], own)

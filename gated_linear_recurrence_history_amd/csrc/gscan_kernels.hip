@@ -870,10 +870,18 @@ gscan_fwd_ms_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
             aA[s] = zero4();
             aB[s] = zero4();
         }
+        // unit q + 1 is split (and its register slot refilled with the next
+        // block's unit) in the same stretch as unit q's products, so the
+        // split's vector work can issue while the matrix cores run
+        Split hn = blk.op(0);
+        blk.load_unit(nrow, kg, 0);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const Split h = blk.op(q);
-            blk.load_unit(nrow, kg, q);
+            const Split h = hn;
+            if (q + 1 < NQ) {
+                hn = blk.op(q + 1);
+                blk.load_unit(nrow, kg, q + 1);
+            }
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 aA[s] = mfma3<LO>(h, img_op(img, (s * NQ + q) * 2, lane), aA[s]);

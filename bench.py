@@ -44,7 +44,8 @@ Fields beyond the headline value:
                     same workload on this host's cores
   configs           every named workload (tiny, headline, long K, bf16 big
                     batch, wide): forward and backward HIP-event time per call
-                    on resident synthetic inputs, samples/s, the fraction
+                    (median of three batches) on resident synthetic inputs,
+                    samples/s, the fraction
                     of 8 TB/s their algorithmic bytes reach, and the step's
                     floor (per pass the higher of its HBM and MFMA times) as
                     a fraction of its time
@@ -298,9 +299,10 @@ def cifg(stream, reps):
 
 def all_configs(stream, workloads=None):
     """Forward and backward per call on every named workload: one input set
-    each, at least 20 calls per figure.  The tiny and headline sets fit in
-    the 256 MB Infinity Cache, so their figures here are cache-warm (the
-    headline line above rotates input sets); the larger sets exceed it."""
+    each, the median of three batches of at least 20 calls per figure.  The
+    tiny and headline sets fit in the 256 MB Infinity Cache, so their figures
+    here are cache-warm (the headline line above rotates input sets); the
+    larger sets exceed it."""
     import numpy as np
     import torch
 
@@ -326,15 +328,20 @@ def all_configs(stream, workloads=None):
         for name, fn in (("fwd", f), ("bwd", b)):
             for _ in range(3):
                 fn()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times[name] = e0.elapsed_time(e1) * 1e3 / reps
+            # the median of three timed batches, so that one stall of the
+            # device (a clock change, another process) does not set the figure
+            per = []
+            for _ in range(3):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(reps):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) * 1e3 / reps)
+            times[name] = sorted(per)[1]
         tot = times["fwd"] + times["bwd"]
         byts = w.fwd_bytes() + w.bwd_bytes()
         # the step's floor: per pass the higher of its HBM time at 8 TB/s and
@@ -347,7 +354,7 @@ def all_configs(stream, workloads=None):
                        "samples_per_s": round(w.B / (tot * 1e-6), 1),
                        "hbm_frac": round(byts / (tot * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
                        "floor_us": round(floor, 2), "frac_of_floor": round(floor / tot, 4),
-                       "reps": reps}
+                       "reps": reps, "batches": 3}
         del t, ctx, dW, ws
         torch.cuda.empty_cache()
     return res

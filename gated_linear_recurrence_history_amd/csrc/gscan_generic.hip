@@ -50,8 +50,8 @@ hipError_t gen_forward(const Plan &p, const void *hh, const void *hs2, const flo
                        const float *WB, const float *WC, float a_shift, const CtxOut &ctx,
                        float *ab, float *cv, hipStream_t st)
 {
-    hipError_t e = launch_proj(p.dtype, hh, WA, WB, p.D, p.SH2, 2 * p.D, p.B * p.K, ab, st);
-    if (e == hipSuccess) e = launch_proj(p.dtype, hs2, WC, nullptr, p.D, p.SH2, p.D, p.B, cv, st);
+    hipError_t e = launch_proj_ab_c(p.dtype, hh, hs2, WA, WB, WC, p.B * p.K, p.B, p.SH2, p.D, ab,
+                                    cv, st);
     if (e != hipSuccess) return e;
     const int64_t n = p.B * p.D;
     const int64_t blocks = (n + kGenThreads - 1) / kGenThreads;
@@ -76,8 +76,8 @@ hipError_t launch_gen_partials(const Plan &p, const void *hh, const void *hs2, c
 {
     // replayed projections, the exact adjoints in place, then the
     // contractions of Backward Step 3 into the slab partials
-    hipError_t e = launch_proj(p.dtype, hh, WA, WB, p.D, p.SH2, 2 * p.D, p.B * p.K, ab, st);
-    if (e == hipSuccess) e = launch_proj(p.dtype, hs2, WC, nullptr, p.D, p.SH2, p.D, p.B, cv, st);
+    hipError_t e = launch_proj_ab_c(p.dtype, hh, hs2, WA, WB, WC, p.B * p.K, p.B, p.SH2, p.D, ab,
+                                    cv, st);
     if (e == hipSuccess) e = launch_adjoint(p, ab, cv, dctx, a_shift, st);
     if (e == hipSuccess) e = launch_gen_contract(p, hh, hs2, ab, cv, part, st);
     return e;

@@ -95,6 +95,12 @@ hipError_t launch_gen_partials(const Plan &p, const void *hh, const void *hs2, c
 hipError_t launch_proj(int dtype, const void *in, const float *W1, const float *W2, int64_t D1,
                        int64_t KD, int64_t NOUT, int64_t nrows, float *out, hipStream_t stream);
 
+// Both: ab [rows][2D] = h_history [W_A | W_B] and cv [B][D] = h_s2 W_C, in
+// one launch where the slice widths allow.
+hipError_t launch_proj_ab_c(int dtype, const void *hh, const void *hs2, const float *WA,
+                            const float *WB, const float *WC, int64_t rows, int64_t B,
+                            int64_t SH2, int64_t D, float *ab, float *cv, hipStream_t stream);
+
 // The weight-gradient contractions of the materialised-projection path into
 // p.gen_slabs partials: h_history^T [dA | dB] (ab [B*K][2D]) and h_s2^T dC
 // (cv [B][D]).

@@ -2733,7 +2733,7 @@ template <typename TIn, int CT, int WT>
 __device__ __forceinline__ void
 rows_by_weights(const TIn *__restrict__ in, const float *__restrict__ W1,
                 const float *__restrict__ W2, int D1, int KD, int NOUT, int64_t nrows,
-                float *__restrict__ out)
+                float *__restrict__ out, int64_t bid, int64_t nblk)
 {
     constexpr bool LO = !std::is_same<TIn, uint16_t>::value;
     extern __shared__ u4 img[];  // [kc][ct][hi, lo][lane]
@@ -2743,12 +2743,14 @@ rows_by_weights(const TIn *__restrict__ in, const float *__restrict__ W1,
     const int nkc = (KD + 31) / 32;
     // 1-D persistent grid of (row tile, column slice) pairs, XCD-aware: the
     // slices of one row tile run on one XCD at about the same time, so the
-    // tile comes from HBM once and from that XCD's L2 for the other slices
+    // tile comes from HBM once and from that XCD's L2 for the other slices.
+    // bid: this workgroup's index among the nblk of its launch (or of its
+    // part of a launch, which starts at a multiple of the XCD count).
     const int nsl = NOUT / (16 * CT);
-    int64_t t0;
-    int slice;
-    decode_block(nsl, t0, slice);
-    const int64_t tstride = (int64_t)gridDim.x / nsl;
+    const int64_t rest = bid / kXcds;
+    const int slice = (int)(rest % nsl);
+    const int64_t t0 = (rest / nsl) * kXcds + bid % kXcds;
+    const int64_t tstride = nblk / nsl;
     const int c0 = slice * CT * 16;
     for (int e0 = tid; e0 < nkc * CT * kWave; e0 += kThreads) {
         const int l = e0 & (kWave - 1), ct = (e0 / kWave) % CT, kc = e0 / kWave / CT;
@@ -2879,7 +2881,7 @@ gscan_dinput_kernel(const float *__restrict__ in, const float *__restrict__ W1,
                     const float *__restrict__ W2, int D1, int KD, int SH2, int64_t nrows,
                     float *__restrict__ out)
 {
-    rows_by_weights<float, CT, kWDin>(in, W1, W2, D1, KD, SH2, nrows, out);
+    rows_by_weights<float, CT, kWDin>(in, W1, W2, D1, KD, SH2, nrows, out, blockIdx.x, gridDim.x);
 }
 
 // WHICH: 0 for [A | Bv] from h_history, 1 for C from h_s2 (profile names)
@@ -2889,7 +2891,34 @@ gscan_proj_kernel(const TIn *__restrict__ in, const float *__restrict__ W1,
                   const float *__restrict__ W2, int D1, int KD, int NOUT, int64_t nrows,
                   float *__restrict__ out)
 {
-    rows_by_weights<TIn, CT, kWProj>(in, W1, W2, D1, KD, NOUT, nrows, out);
+    rows_by_weights<TIn, CT, kWProj>(in, W1, W2, D1, KD, NOUT, nrows, out, blockIdx.x,
+                                     gridDim.x);
+}
+
+// Both projections of Forward Step 1 in one launch: workgroups [0, nwg0)
+// form [A | Bv] (job 0, CT0 output tiles per slice), the rest C (job 1,
+// CT1), so that the small C projection runs beside the large one instead
+// of after it.
+struct ProjJob {
+    const void *in;
+    const float *W1, *W2;
+    int D1, KD, NOUT;
+    int64_t nrows;
+    float *out;
+};
+
+template <typename TIn, int CT0, int CT1>
+__global__ void __launch_bounds__(kThreads)
+gscan_proj2_kernel(ProjJob j0, ProjJob j1, int64_t nwg0)
+{
+    const int64_t b = blockIdx.x;
+    if (b < nwg0)
+        rows_by_weights<TIn, CT0, kWProj>(static_cast<const TIn *>(j0.in), j0.W1, j0.W2, j0.D1,
+                                          j0.KD, j0.NOUT, j0.nrows, j0.out, b, nwg0);
+    else
+        rows_by_weights<TIn, CT1, kWProj>(static_cast<const TIn *>(j1.in), j1.W1, j1.W2, j1.D1,
+                                          j1.KD, j1.NOUT, j1.nrows, j1.out, b - nwg0,
+                                          (int64_t)gridDim.x - nwg0);
 }
 
 // ----------------------------------------------------------------- dispatch
@@ -3311,6 +3340,53 @@ hipError_t launch_proj_which(const TIn *in, const float *W1, const float *W2, in
     default: hipLaunchKernelGGL((gscan_proj_kernel<TIn, 1, WHICH>), grid, dim3(kThreads), shmem, st, in, W1, W2, d1, kd, no, nrows, out); break;
     }
     return hipGetLastError();
+}
+
+namespace {
+template <typename TIn, int CT0>
+hipError_t proj2_ct1(const ProjJob &j0, const ProjJob &j1, const RbwShape &s0,
+                     const RbwShape &s1, hipStream_t st)
+{
+    const size_t shmem = s0.shmem > s1.shmem ? s0.shmem : s1.shmem;
+    const dim3 grid(s0.grid.x + s1.grid.x);
+    const int64_t nwg0 = s0.grid.x;
+    if (s1.ct == CT0)
+        hipLaunchKernelGGL((gscan_proj2_kernel<TIn, CT0, CT0>), grid, dim3(kThreads), shmem, st,
+                           j0, j1, nwg0);
+    else if constexpr (CT0 >= 2)
+        hipLaunchKernelGGL((gscan_proj2_kernel<TIn, CT0, CT0 / 2>), grid, dim3(kThreads), shmem,
+                           st, j0, j1, nwg0);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t proj2(const ProjJob &j0, const ProjJob &j1, const RbwShape &s0, const RbwShape &s1,
+                 hipStream_t st)
+{
+    switch (s0.ct) {
+    case 16: return proj2_ct1<TIn, 16>(j0, j1, s0, s1, st);
+    case 8: return proj2_ct1<TIn, 8>(j0, j1, s0, s1, st);
+    case 4: return proj2_ct1<TIn, 4>(j0, j1, s0, s1, st);
+    case 2: return proj2_ct1<TIn, 2>(j0, j1, s0, s1, st);
+    default: return proj2_ct1<TIn, 1>(j0, j1, s0, s1, st);
+    }
+}
+}  // namespace
+
+hipError_t launch_proj_ab_c(int dtype, const void *hh, const void *hs2, const float *WA,
+                            const float *WB, const float *WC, int64_t rows, int64_t B,
+                            int64_t SH2, int64_t D, float *ab, float *cv, hipStream_t st)
+{
+    const RbwShape s0 = rbw_shape(SH2, 2 * D, rows), s1 = rbw_shape(SH2, D, B);
+    if (s1.ct != s0.ct && 2 * s1.ct != s0.ct) {
+        // slice widths the combined kernel is not compiled for: two launches
+        hipError_t e = launch_proj(dtype, hh, WA, WB, D, SH2, 2 * D, rows, ab, st);
+        if (e == hipSuccess) e = launch_proj(dtype, hs2, WC, nullptr, D, SH2, D, B, cv, st);
+        return e;
+    }
+    const ProjJob j0 = {hh, WA, WB, (int)D, (int)SH2, (int)(2 * D), rows, ab};
+    const ProjJob j1 = {hs2, WC, nullptr, (int)D, (int)SH2, (int)D, B, cv};
+    return dtype == 1 ? proj2<uint16_t>(j0, j1, s0, s1, st) : proj2<float>(j0, j1, s0, s1, st);
 }
 
 hipError_t launch_proj(int dtype, const void *in, const float *W1, const float *W2, int64_t D1,

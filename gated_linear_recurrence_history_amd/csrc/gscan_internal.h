@@ -49,7 +49,7 @@ struct Plan {
     // the forward needs fwd_scratch bytes (A | Bv, then C at fwd_cv).
     bool generic = false;
     int64_t gen_slabs = 0;
-    int gen_mt = 0, gen_nt_ab = 0, gen_nt_c = 0;  // contraction tile (h columns, outputs)
+    int gen_mt = 0, gen_nt_ab = 0;  // contraction tile (h columns, outputs), both contractions
     size_t fwd_scratch = 0, fwd_cv = 0;
     int64_t split_slabs = 0;
     int64_t ps_grid = 0;

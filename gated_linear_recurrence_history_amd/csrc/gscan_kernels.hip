@@ -2462,13 +2462,12 @@ constexpr int kCtRows = 32;
 // WHICH0: the partial the first output column goes to (0: dW_A, then dW_B;
 // 2: dW_C), fixed at compile time so that the two launches are told apart
 // in profiles.
-template <typename TX, int MT, int NT, int WN, int WHICH0>
-__global__ void __launch_bounds__(kCtThreads, 1)
-gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__restrict__ Y, int ldy,
-                          int64_t rows, int64_t rows_per_slab, int D, int SH2,
-                          float *__restrict__ part)
+template <typename TX, int MT, int NT, int WN>
+__device__ __forceinline__ void
+contract_slab(const TX *__restrict__ X, int ldx, const float *__restrict__ Y, int ldy,
+              int64_t rows, int64_t rows_per_slab, int D, int SH2, float *__restrict__ part,
+              int which0, int64_t slab, int mt, int nt)
 {
-    constexpr int which0 = WHICH0;
     constexpr bool LO = !std::is_same<TX, uint16_t>::value;
     constexpr int kPl = LO ? 2 : 1;               // planes of X
     // LDS row pitches (bf16): a transposed read takes 32 bytes of each of
@@ -2487,8 +2486,7 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
     const int lane = tid & 63, wave = wave_id();
     const int kg = lane >> 4, ln = lane & 15;
     const int wm = wave % WM, wn = wave / WM;
-    const int64_t slab = blockIdx.x;
-    const int m0 = blockIdx.y * MT, n0 = blockIdx.z * NT;
+    const int m0 = mt * MT, n0 = nt * NT;
     const int64_t r_begin = slab * rows_per_slab;
     const int64_t r_end = r_begin + rows_per_slab < rows ? r_begin + rows_per_slab : rows;
 
@@ -2621,6 +2619,45 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
                 if (ii < SH2) P[((int64_t)which * SH2 + ii) * D + s] = acc[i][j][e];
             }
         }
+}
+
+template <typename TX, int MT, int NT, int WN, int WHICH0>
+__global__ void __launch_bounds__(kCtThreads, 1)
+gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__restrict__ Y, int ldy,
+                          int64_t rows, int64_t rows_per_slab, int D, int SH2,
+                          float *__restrict__ part)
+{
+    contract_slab<TX, MT, NT, WN>(X, ldx, Y, ldy, rows, rows_per_slab, D, SH2, part, WHICH0,
+                                  blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Both contractions of the materialised-projection path in one launch, on
+// the same tile shape: workgroups [0, nb0) take h_history^T [dA | dB]
+// (job 0, partials 0 and 1), the rest h_s2^T dC (job 1, partial 2); each
+// job's workgroups are ordered (slab, m tile, n tile), slab slowest.
+struct CtJob {
+    const void *X;
+    int ldx;
+    const float *Y;
+    int ldy;
+    int64_t rows, rps;
+    int which0, gm, gn;
+};
+
+template <typename TX, int MT, int NT>
+__global__ void __launch_bounds__(kCtThreads, 1)
+gscan_gen_contract_kernel(CtJob j0, CtJob j1, int64_t nb0, int D, int SH2,
+                          float *__restrict__ part)
+{
+    int64_t b = blockIdx.x;
+    const bool second = b >= nb0;
+    const CtJob &j = second ? j1 : j0;
+    if (second) b -= nb0;
+    const int per = j.gm * j.gn;
+    const int64_t slab = b / per;
+    const int r = (int)(b - slab * per);
+    contract_slab<TX, MT, NT, 4>(static_cast<const TX *>(j.X), j.ldx, j.Y, j.ldy, j.rows, j.rps, D,
+                                 SH2, part, j.which0, slab, r / j.gn, r % j.gn);
 }
 
 // ================================================= phase 2: partial reduction
@@ -3141,7 +3178,6 @@ bool make_plan(int64_t B, int64_t K, int64_t SH2, int64_t D, int dtype, Plan *p)
         auto pick = [](int64_t n, int64_t a, int64_t b) { return (n + a - 1) / a * a < (n + b - 1) / b * b ? a : b; };
         q.gen_mt = (int)pick(SH2, 128, 256);
         q.gen_nt_ab = (int)pick(2 * D, 64, 128);
-        q.gen_nt_c = (int)pick(D, 64, 128);
         const int64_t tiles = (SH2 + q.gen_mt - 1) / q.gen_mt * ((2 * D + q.gen_nt_ab - 1) / q.gen_nt_ab);
         const int64_t rows = B * K;
         int64_t slabs = 256 / tiles;
@@ -3400,31 +3436,6 @@ hipError_t launch_proj(int dtype, const void *in, const float *W1, const float *
               : launch_proj_which<float, 1>(static_cast<const float *>(in), W1, W2, D1, KD, NOUT, nrows, out, st);
 }
 
-namespace {
-template <typename TX, int MT, int NT, int WHICH0>
-hipError_t contract_tiles(const Plan &p, const TX *X, const float *Y, int ldy, int64_t rows,
-                          int64_t rps, float *part, hipStream_t st)
-{
-    const dim3 grid((unsigned)p.gen_slabs, (unsigned)((p.SH2 + MT - 1) / MT),
-                    (unsigned)((ldy + NT - 1) / NT));
-    hipLaunchKernelGGL((gscan_bwd_contract_kernel<TX, MT, NT, 4, WHICH0>), grid,
-                       dim3(kCtThreads), 0, st, X, (int)p.SH2, Y, ldy, rows, rps, (int)p.D,
-                       (int)p.SH2, part);
-    return hipGetLastError();
-}
-
-template <typename TX, int WHICH0>
-hipError_t contract_any(const Plan &p, const TX *X, const float *Y, int ldy, int64_t rows,
-                        int64_t rps, float *part, hipStream_t st)
-{
-    const bool m256 = p.gen_mt == 256, n128 = (WHICH0 == 0 ? p.gen_nt_ab : p.gen_nt_c) == 128;
-    if (m256 && n128) return contract_tiles<TX, 256, 128, WHICH0>(p, X, Y, ldy, rows, rps, part, st);
-    if (m256) return contract_tiles<TX, 256, 64, WHICH0>(p, X, Y, ldy, rows, rps, part, st);
-    if (n128) return contract_tiles<TX, 128, 128, WHICH0>(p, X, Y, ldy, rows, rps, part, st);
-    return contract_tiles<TX, 128, 64, WHICH0>(p, X, Y, ldy, rows, rps, part, st);
-}
-}  // namespace
-
 hipError_t launch_gen_contract(const Plan &p, const void *hh, const void *hs2, const float *ab,
                                const float *cv, float *part, hipStream_t st)
 {
@@ -3433,17 +3444,29 @@ hipError_t launch_gen_contract(const Plan &p, const void *hh, const void *hs2, c
     const int64_t rps = ((rows + p.gen_slabs - 1) / p.gen_slabs + kCtRows - 1) / kCtRows * kCtRows;
     const int64_t rpsc = (p.B + p.gen_slabs - 1) / p.gen_slabs;
     const int d2 = (int)(2 * p.D), d = (int)p.D;
-    hipError_t e;
+    const int MT = p.gen_mt, NT = p.gen_nt_ab;  // one tile shape for both jobs
+    const int gm = (int)((p.SH2 + MT - 1) / MT);
+    const CtJob j0 = {hh, (int)p.SH2, ab, d2, rows, rps, 0, gm, (d2 + NT - 1) / NT};
+    const CtJob j1 = {hs2, (int)p.SH2, cv, d, p.B, rpsc, 2, gm, (d + NT - 1) / NT};
+    const int64_t nb0 = p.gen_slabs * j0.gm * j0.gn, nb1 = p.gen_slabs * j1.gm * j1.gn;
+    const dim3 grid((unsigned)(nb0 + nb1));
+    const int sh2 = (int)p.SH2;
+#define GSCAN_GEN_CT(TX, MTV, NTV)                                                              \
+    hipLaunchKernelGGL((gscan_gen_contract_kernel<TX, MTV, NTV>), grid, dim3(kCtThreads), 0, st, \
+                       j0, j1, nb0, d, sh2, part)
     if (p.dtype == 1) {
-        e = contract_any<uint16_t, 0>(p, static_cast<const uint16_t *>(hh), ab, d2, rows, rps, part, st);
-        if (e == hipSuccess)
-            e = contract_any<uint16_t, 2>(p, static_cast<const uint16_t *>(hs2), cv, d, p.B, rpsc, part, st);
+        if (MT == 256 && NT == 128) GSCAN_GEN_CT(uint16_t, 256, 128);
+        else if (MT == 256) GSCAN_GEN_CT(uint16_t, 256, 64);
+        else if (NT == 128) GSCAN_GEN_CT(uint16_t, 128, 128);
+        else GSCAN_GEN_CT(uint16_t, 128, 64);
     } else {
-        e = contract_any<float, 0>(p, static_cast<const float *>(hh), ab, d2, rows, rps, part, st);
-        if (e == hipSuccess)
-            e = contract_any<float, 2>(p, static_cast<const float *>(hs2), cv, d, p.B, rpsc, part, st);
+        if (MT == 256 && NT == 128) GSCAN_GEN_CT(float, 256, 128);
+        else if (MT == 256) GSCAN_GEN_CT(float, 256, 64);
+        else if (NT == 128) GSCAN_GEN_CT(float, 128, 128);
+        else GSCAN_GEN_CT(float, 128, 64);
     }
-    return e;
+#undef GSCAN_GEN_CT
+    return hipGetLastError();
 }
 
 hipError_t launch_dinput(const float *in, const float *W1, const float *W2, int64_t D1, int64_t KD,

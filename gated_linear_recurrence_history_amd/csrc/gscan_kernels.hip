@@ -3309,21 +3309,26 @@ hipError_t launch_adjoint(const Plan &p, float *ab, float *cv, const float *dctx
 }
 
 // Launch shape of rows_by_weights: the widest column slice (CT tiles of 16)
-// whose weight image fits (<= 64 KiB), narrowed while there are too few
-// (row tile, slice) pairs to fill the chip.
+// whose weight image fits (max_pairs (k chunk, tile) pairs of 2 KiB),
+// narrowed while there are too few (row tile, slice) pairs to fill the chip.
+// The projections take images up to 128 KiB (one workgroup per CU, but each
+// long row split and read once instead of once per slice); the input
+// gradients, whose rows are short and whose time is their output stream,
+// keep two workgroups per CU (64 KiB).
 struct RbwShape {
     int ct;
     size_t shmem;
     dim3 grid;
 };
 
-RbwShape rbw_shape(int64_t KD, int64_t NOUT, int64_t nrows)
+RbwShape rbw_shape(int64_t KD, int64_t NOUT, int64_t nrows, int max_pairs)
 {
     const int nkc = (int)((KD + 31) / 32);
     const int tiles16 = (int)(NOUT / 16);
     const int64_t row_tiles = (nrows + kDinRows - 1) / kDinRows;
     int ct = 16;
-    while (ct > 1 && (ct * nkc > 32 || tiles16 % ct != 0 || row_tiles * (tiles16 / ct) < kDinMaxWorkgroups))
+    while (ct > 1 && (ct * nkc > max_pairs || tiles16 % ct != 0 ||
+                      row_tiles * (tiles16 / ct) < kDinMaxWorkgroups))
         ct /= 2;
     RbwShape r;
     r.ct = ct;
@@ -3345,7 +3350,7 @@ hipError_t launch_dinput_which(const float *in, const float *W1, const float *W2
                                int64_t KD, int64_t SH2, int64_t nrows, float *out, hipStream_t st)
 {
     if (nrows <= 0) return hipSuccess;
-    const RbwShape sh = rbw_shape(KD, SH2, nrows);
+    const RbwShape sh = rbw_shape(KD, SH2, nrows, 32);
     const dim3 grid = sh.grid;
     const size_t shmem = sh.shmem;
     const int d1 = (int)D1, kd = (int)KD, sh2 = (int)SH2;
@@ -3364,7 +3369,7 @@ hipError_t launch_proj_which(const TIn *in, const float *W1, const float *W2, in
                              int64_t KD, int64_t NOUT, int64_t nrows, float *out, hipStream_t st)
 {
     if (nrows <= 0) return hipSuccess;
-    const RbwShape sh = rbw_shape(KD, NOUT, nrows);
+    const RbwShape sh = rbw_shape(KD, NOUT, nrows, 64);
     const dim3 grid = sh.grid;
     const size_t shmem = sh.shmem;
     const int d1 = (int)D1, kd = (int)KD, no = (int)NOUT;
@@ -3413,7 +3418,7 @@ hipError_t launch_proj_ab_c(int dtype, const void *hh, const void *hs2, const fl
                             const float *WB, const float *WC, int64_t rows, int64_t B,
                             int64_t SH2, int64_t D, float *ab, float *cv, hipStream_t st)
 {
-    const RbwShape s0 = rbw_shape(SH2, 2 * D, rows), s1 = rbw_shape(SH2, D, B);
+    const RbwShape s0 = rbw_shape(SH2, 2 * D, rows, 64), s1 = rbw_shape(SH2, D, B, 64);
     if (s1.ct != s0.ct && 2 * s1.ct != s0.ct) {
         // slice widths the combined kernel is not compiled for: two launches
         hipError_t e = launch_proj(dtype, hh, WA, WB, D, SH2, 2 * D, rows, ab, st);

@@ -3,12 +3,13 @@
 // structure of the design spec "Custom Kernel Optimization - cuBLAS
 // Projections + Batch-Parallel Scans", Design 1: the projections of
 // Forward Step 1 written to a scratch buffer (split-bf16 products on the
-// matrix cores, gscan_proj_kernel), then the lightweight scan with one
-// thread per (sample, state); for the backward, the replayed projections,
-// the reverse scan (the per-sample adjoint pass shared with the general
-// kernel) and the weight-gradient contractions of Backward Step 3 into
-// per-slab partials (the split backward's contraction kernel, with ragged
-// tiles), summed by the fixed-order reduction.
+// matrix cores, both projections in one launch: gscan_proj2_kernel), then
+// the lightweight scan with one thread per (sample, state); for the
+// backward, the replayed projections, the reverse scan (the per-sample
+// adjoint pass shared with the general kernel) and the weight-gradient
+// contractions of Backward Step 3 into per-slab partials (the split
+// backward's contraction loop with ragged tiles, both contractions in one
+// launch: gscan_gen_contract_kernel), summed by the fixed-order reduction.
 #include <cstdint>
 
 #include "gscan_internal.h"

@@ -89,15 +89,16 @@ def test_input_grad_parity(case):
         assert np.array_equal(g, r)
 
 
-@pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
+@pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS + wl.OUT_OF_ENVELOPE])
 def test_input_grad_full_size(name):
-    """Each named workload at full size in the benchmark's launch
+    """Each named workload, and the headline shape at the two out-of-envelope
+    widths, at full size in the benchmark's launch
     configuration: every element of d_h_history and d_h_s2 against the
     oracle, except for the wide workload (2^21 rows of 512: hours of host
     time for the fp64 oracle), where the rows of 64 sampled samples are
     compared (a sample's input gradients depend on that sample alone); and
     <h_s2, dL/dh_s2> = L over the whole batch (L is linear in h_s2)."""
-    w = wl.BY_NAME[name]
+    w = next(c for c in wl.WORKLOADS + wl.OUT_OF_ENVELOPE if c.name == name)
     tol = wl.tolerance(w)
     print(f"case input grads full {w.name} B={w.B} K={w.K} SH2={w.SH2} D={w.D}", flush=True)
     x = synth.make_inputs(w)

@@ -21,6 +21,8 @@ Fields beyond the headline value:
                     forward runs on set i (the backward's set was last read
                     six passes, 432 MiB, earlier): time per step, samples/s,
                     fraction of 8 TB/s and of the read ceiling
+  graph_ms_per_step the same steps captured once as a HIP graph (one step
+                    per input set) and replayed, time per step
   step_us           p10 / p50 / p90 of single-step times (an event pair
                     around each step, measured after the timed region)
   copy_GBs          a streaming figure for context: bytes read plus written
@@ -558,6 +560,38 @@ def main():
         torch.cuda.synchronize()
         nr_ms = r0.elapsed_time(r1) / args.steps
 
+    # ---- the same steps captured once as a HIP graph (one step per input
+    # set, the calls prepared on the capture stream) and replayed: what the
+    # per-call host work and the launch gaps cost the eager loop
+    graph_ms = None
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        cap = torch.cuda.current_stream(dev)
+        gsteps = []
+        for t in sets:
+            a = (t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], w.K)
+            gsteps.append((binding.prepare_forward(*a, ctx, w.a_shift, cap),
+                           binding.prepare_backward(*a, t["d_context"], dW, ws, w.a_shift, cap)))
+        for f_, b_ in gsteps:
+            f_()
+            b_()
+    torch.cuda.synchronize()
+    greps = max(1, args.steps // n)
+    g.replay()
+    torch.cuda.synchronize()
+    q0 = torch.cuda.Event(enable_timing=True)
+    q1 = torch.cuda.Event(enable_timing=True)
+    q0.record(stream)
+    for _ in range(greps):
+        g.replay()
+    q1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = q0.elapsed_time(q1) / (greps * n)
+    del g
+
     # ---- per-kernel durations: each kernel launched back to back on the same
     # stream (rotating the input sets), HIP events around the whole run
     reps = max(20, min(args.steps, 200))
@@ -674,6 +708,7 @@ def main():
             "hbm_frac": round(step_bytes / (nr_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "frac_of_read_ceiling": round(step_bytes / (nr_ms * 1e-3) / 1e9 / rd_gbs, 4),
             "backward_set_offset": 2},
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "step_us": step_us,
         "copy_GBs": round(copy_gbs, 1),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 5),

@@ -2726,24 +2726,56 @@ gscan_adjoint_kernel(float *__restrict__ ab, float *__restrict__ cv,
     const int64_t b = i / D;
     const int s = (int)(i - b * D);
     float *base = ab + b * K * 2 * D + s;
+    // Steps in chunks of kC: a chunk's loads all go out before its stores
+    // (which overwrite slots the chunk has already read), so the loads of
+    // a chunk are in flight together instead of one step at a time.
+    constexpr int kC = 8;
     float x = 0.f;
-    for (int64_t t = 0; t < K; ++t) {
-        float *row = base + t * 2 * D;
-        const float g = sigmoid(row[0] + a_shift);
-        const float bv = row[D];
-        row[D] = x;  // x_t
-        x = g * x + bv;
+    for (int64_t t0 = 0; t0 < K; t0 += kC) {
+        const int n = K - t0 < kC ? (int)(K - t0) : kC;
+        float av[kC], bv[kC];
+#pragma unroll
+        for (int u = 0; u < kC; ++u) {
+            if (u < n) {
+                const float *row = base + (t0 + u) * 2 * D;
+                av[u] = row[0];
+                bv[u] = row[D];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kC; ++u) {
+            if (u < n) {
+                const float g = sigmoid(av[u] + a_shift);
+                base[(t0 + u) * 2 * D + D] = x;  // x_t
+                x = g * x + bv[u];
+            }
+        }
     }
     const float d = dctx[i];
     float lam = d * cv[i];
     cv[i] = d * x;  // dL/dC = d_context * x_K
-    for (int64_t t = K - 1; t >= 0; --t) {
-        float *row = base + t * 2 * D;
-        const Gate gg = gate_of(row[0] + a_shift);
-        const float xt = row[D];
-        row[D] = lam;                           // dL/dBv_t
-        row[0] = lam * xt * (gg.g * gg.gc);     // dL/dA_t
-        lam = gg.g * lam;
+    for (int64_t t1 = K; t1 > 0; t1 -= kC) {
+        const int n = t1 < kC ? (int)t1 : kC;
+        const int64_t t0 = t1 - n;
+        float av[kC], xv[kC];
+#pragma unroll
+        for (int u = 0; u < kC; ++u) {
+            if (u < n) {
+                const float *row = base + (t0 + u) * 2 * D;
+                av[u] = row[0];
+                xv[u] = row[D];
+            }
+        }
+#pragma unroll
+        for (int u = kC - 1; u >= 0; --u) {
+            if (u < n) {
+                float *row = base + (t0 + u) * 2 * D;
+                const Gate gg = gate_of(av[u] + a_shift);
+                row[D] = lam;                           // dL/dBv_t
+                row[0] = lam * xv[u] * (gg.g * gg.gc);  // dL/dA_t
+                lam = gg.g * lam;
+            }
+        }
     }
 }
 

@@ -2662,13 +2662,16 @@ gscan_gen_contract_kernel(CtJob j0, CtJob j1, int64_t nb0, int D, int SH2,
 
 // ================================================= phase 2: partial reduction
 // Workgroup = 32 consecutive gradient entries; thread (seg, quad) sums rows
-// r = seg, seg+32, ... of four consecutive entries, eight rows in flight at
-// a time; the 32 row segments are then added in segment order.  Fixed order,
+// r = seg, seg+16, ... of four consecutive entries, eight rows in flight at
+// a time; the 16 row segments are then added in segment order.  Fixed order,
 // so bitwise reproducible.
 constexpr int kRedCols = 32;
-constexpr int kRedSegs = kThreads / (kRedCols / 4);
+// 128 threads (16 row segments): a workgroup this small finds room on a CU
+// while the phase-1 workgroups there are still draining
+constexpr int kRedThreads = 128;
+constexpr int kRedSegs = kRedThreads / (kRedCols / 4);
 
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kRedThreads)
 gscan_reduce_kernel(const float *__restrict__ part, int64_t nrows, int64_t wsz, int D, int qlay,
                     float *__restrict__ dWA, float *__restrict__ dWB, float *__restrict__ dWC)
 {
@@ -3518,7 +3521,7 @@ hipError_t launch_backward_reduce(const Plan &p, const float *part, float *dWA, 
 {
     // the per-block kernel writes its partials in the quad layout; the
     // general kernel and the split contraction in [which][i][s]
-    hipLaunchKernelGGL(gscan_reduce_kernel, dim3((unsigned)p.red_grid), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(gscan_reduce_kernel, dim3((unsigned)p.red_grid), dim3(kRedThreads), 0, st,
                        part, p.bwd_rows, p.SH2 * p.D, (int)p.D, p.bwd_rows_kernel ? 1 : 0, dWA,
                        dWB, dWC);
     return hipGetLastError();

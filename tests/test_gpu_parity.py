@@ -104,6 +104,11 @@ SMALL = [
     (600, 4, 48, 16, "f32", 2.0),
     (3000, 8, 80, 32, "f32", 0.0),
     (1, 1, 16, 16, "f32", -3.0),
+    # very long scans: a sample spans many chunks and tiles of every route
+    (2, 4096, 64, 16, "f32", 1.5),
+    (1, 20000, 128, 16, "f32", 2.0),
+    (3, 1000, 96, 32, "f32", 1.0),
+    (2, 3000, 320, 48, "bf16", 2.5),
 ]
 
 

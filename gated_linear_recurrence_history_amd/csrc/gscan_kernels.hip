@@ -43,6 +43,25 @@
 // lane groups (l/16) combine with two shuffle steps, wavefronts through LDS.
 // The backward runs the same construction on the reverse adjoint
 //   mu_{r-1} = g_r * mu_r (t_r > 0),   mu_{r-1} = lambda_K(previous sample) (t_r = 0).
+//
+// Kernels in this file (the launch plan, make_plan, picks among them):
+//   gscan_fwd_kernel, gscan_fwd_persist_kernel  forward, one group x one slice
+//   gscan_fwd_ms_kernel      forward, two groups x S slices sharing each split row
+//   gscan_fwd_rows_kernel, gscan_bwd_rows_kernel  the per-block decomposition
+//                            (rows_pass: 4 row blocks x 2 column halves, persistent;
+//                            K dividing 16, or 32, 64; SH2 <= 256), the backward
+//                            optionally with the input gradients
+//   gscan_bwd_kernel         the general backward (any K)
+//   gscan_bwd_scan_kernel, gscan_fwd_tile_kernel, gscan_bwd_contract_kernel
+//                            SH2 = 512 over 256-row tiles: scan pass, tile forward,
+//                            contraction over row slabs
+//   gscan_reduce_kernel      phase 2: fixed-order sum of the partials
+//   gscan_adjoint_kernel     exact adjoints from stored projections
+//   gscan_dinput_kernel, gscan_proj_kernel, gscan_proj2_kernel  rows x weights
+//                            (rows_by_weights): input-gradient products and the
+//                            projections written out for the shapes outside the
+//                            fused kernels
+//   gscan_gen_contract_kernel  those shapes' weight-gradient contractions
 #include <cstdint>
 #include <type_traits>
 

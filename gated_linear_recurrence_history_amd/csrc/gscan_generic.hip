@@ -33,10 +33,26 @@ gscan_gen_fwd_scan_kernel(const float *__restrict__ ab, const float *__restrict_
         const int s = (int)(e % D);
         const float *row = ab + b * K * 2 * D;
         float x = 0.f;
-        for (int64_t t = 0; t < K; ++t) {
-            const float a = row[t * 2 * D + s] + a_shift;
-            const float g = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
-            x = g * x + row[t * 2 * D + D + s];
+        // steps in chunks of kC whose loads all go out before the chunk's
+        // arithmetic, so that they are in flight together
+        constexpr int kC = 8;
+        for (int64_t t0 = 0; t0 < K; t0 += kC) {
+            const int n = K - t0 < kC ? (int)(K - t0) : kC;
+            float av[kC], bv[kC];
+#pragma unroll
+            for (int u = 0; u < kC; ++u) {
+                if (u < n) {
+                    av[u] = row[(t0 + u) * 2 * D + s];
+                    bv[u] = row[(t0 + u) * 2 * D + D + s];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kC; ++u) {
+                if (u < n) {
+                    const float g = __builtin_amdgcn_rcpf(1.0f + __expf(-(av[u] + a_shift)));
+                    x = g * x + bv[u];
+                }
+            }
         }
         const float v = cv[b * D + s] * x;
         if (out.ctx) out.ctx[b * D + s] = v;

@@ -30,7 +30,7 @@ Fields beyond the headline value:
                     of 5)
   kernels_us        average duration of each kernel: HIP events on the
                     launch stream around a run of back-to-back launches of
-                    that kernel alone
+                    that kernel alone (the median of three such runs)
   roofline          the dominant (longest) kernel against the roof that
                     bounds it (the higher of its HBM floor and its MFMA
                     floor): algorithmic bytes per launch over its average
@@ -597,14 +597,19 @@ def main():
     reps = max(20, min(args.steps, 200))
 
     def per_launch_us(fn):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(reps):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / reps
+        # the median of three timed runs, so that one stall of the device
+        # does not set the figure
+        per = []
+        for _ in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(reps):
+                fn(i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) * 1e3 / reps)
+        return sorted(per)[1]
 
     for i in range(n):  # workspace holds partials of set i before each reduce
         bwd1[i]()

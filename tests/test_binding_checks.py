@@ -46,3 +46,23 @@ def test_workspace_checks():
         binding._check_workspace(torch.zeros(128, dtype=torch.uint8)[::2], 64, CPU)
     with pytest.raises(ValueError):
         binding._check_workspace(torch.zeros(64, dtype=torch.uint8, device="meta"), 64, CPU)
+
+
+def test_forward_workspace_selection():
+    """The forward's workspace: none where the shape needs none, a caller's
+    tensor checked against the size the library asks for, else one from
+    torch's allocator of exactly that size (the library is only queried for
+    the size, which needs no GPU)."""
+    fused = (64, 8, 256, 16, binding.GSCAN_F32)
+    ptr, n, keep = binding._forward_workspace(None, *fused, CPU)
+    assert ptr is None and n == 0 and keep is None
+    need = binding.forward_workspace_bytes(64, 8, 96, 16)
+    assert need >= 4 * (64 * 8 * 32 + 64 * 16)
+    ptr, n, keep = binding._forward_workspace(None, 64, 8, 96, 16, binding.GSCAN_F32, CPU)
+    assert n == need and keep.numel() == need and ptr == keep.data_ptr()
+    mine = torch.zeros(need, dtype=torch.uint8)
+    ptr, n, keep = binding._forward_workspace(mine, 64, 8, 96, 16, binding.GSCAN_F32, CPU)
+    assert keep is mine and n == need
+    with pytest.raises(ValueError):
+        binding._forward_workspace(torch.zeros(need - 1, dtype=torch.uint8), 64, 8, 96, 16,
+                                   binding.GSCAN_F32, CPU)

@@ -3388,10 +3388,12 @@ RbwShape rbw_shape(int64_t KD, int64_t NOUT, int64_t nrows, int max_pairs)
     r.ct = ct;
     r.shmem = (size_t)nkc * ct * 2 * kWave * sizeof(u4);
     // persistent row-tile slots per slice, a multiple of the XCD count:
-    // about 512 workgroups in all (two per CU), so that each stages its
-    // weight image once for several row tiles
+    // as many workgroups as fit on the chip at once (two per CU; one with an
+    // image above 64 KiB), so that each stages its weight image once for
+    // several row tiles
     const int nsl = tiles16 / ct;
-    int64_t slots = kDinMaxWorkgroups / nsl / kXcds * kXcds;
+    const int64_t wgs = r.shmem > 64 * 1024 ? kDinMaxWorkgroups / 2 : kDinMaxWorkgroups;
+    int64_t slots = wgs / nsl / kXcds * kXcds;
     if (slots < kXcds) slots = kXcds;
     const int64_t need = (row_tiles + kXcds - 1) / kXcds * kXcds;
     if (slots > need) slots = need;

@@ -2651,9 +2651,11 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
 }
 
 // Both contractions of the materialised-projection path in one launch, on
-// the same tile shape: workgroups [0, nb0) take h_history^T [dA | dB]
-// (job 0, partials 0 and 1), the rest h_s2^T dC (job 1, partial 2); each
-// job's workgroups are ordered (slab, m tile, n tile), slab slowest.
+// the same tile shape: workgroup (slab, m tile, n tile), slab slowest, takes
+// that tile of h_history^T [dA | dB] (job 0, partials 0 and 1) and then,
+// where job 1 has the same tile (its outputs are the first D of job 0's
+// 2D), that tile of h_s2^T dC (partial 2) over the slab's samples: one
+// workgroup per CU and no second round for the small job.
 struct CtJob {
     const void *X;
     int ldx;
@@ -2665,18 +2667,19 @@ struct CtJob {
 
 template <typename TX, int MT, int NT>
 __global__ void __launch_bounds__(kCtThreads, 1)
-gscan_gen_contract_kernel(CtJob j0, CtJob j1, int64_t nb0, int D, int SH2,
-                          float *__restrict__ part)
+gscan_gen_contract_kernel(CtJob j0, CtJob j1, int D, int SH2, float *__restrict__ part)
 {
-    int64_t b = blockIdx.x;
-    const bool second = b >= nb0;
-    const CtJob &j = second ? j1 : j0;
-    if (second) b -= nb0;
-    const int per = j.gm * j.gn;
-    const int64_t slab = b / per;
-    const int r = (int)(b - slab * per);
-    contract_slab<TX, MT, NT, 4>(static_cast<const TX *>(j.X), j.ldx, j.Y, j.ldy, j.rows, j.rps, D,
-                                 SH2, part, j.which0, slab, r / j.gn, r % j.gn);
+    const int per = j0.gm * j0.gn;
+    const int64_t slab = blockIdx.x / per;
+    const int r = (int)(blockIdx.x - slab * per);
+    const int mt = r / j0.gn, nt = r % j0.gn;
+    contract_slab<TX, MT, NT, 4>(static_cast<const TX *>(j0.X), j0.ldx, j0.Y, j0.ldy, j0.rows,
+                                 j0.rps, D, SH2, part, j0.which0, slab, mt, nt);
+    if (nt < j1.gn) {  // the same for every thread of the workgroup
+        __syncthreads();  // the tiles' LDS buffers are read to the end first
+        contract_slab<TX, MT, NT, 4>(static_cast<const TX *>(j1.X), j1.ldx, j1.Y, j1.ldy,
+                                     j1.rows, j1.rps, D, SH2, part, j1.which0, slab, mt, nt);
+    }
 }
 
 // ================================================= phase 2: partial reduction
@@ -3509,12 +3512,11 @@ hipError_t launch_gen_contract(const Plan &p, const void *hh, const void *hs2, c
     const int gm = (int)((p.SH2 + MT - 1) / MT);
     const CtJob j0 = {hh, (int)p.SH2, ab, d2, rows, rps, 0, gm, (d2 + NT - 1) / NT};
     const CtJob j1 = {hs2, (int)p.SH2, cv, d, p.B, rpsc, 2, gm, (d + NT - 1) / NT};
-    const int64_t nb0 = p.gen_slabs * j0.gm * j0.gn, nb1 = p.gen_slabs * j1.gm * j1.gn;
-    const dim3 grid((unsigned)(nb0 + nb1));
+    const dim3 grid((unsigned)(p.gen_slabs * j0.gm * j0.gn));
     const int sh2 = (int)p.SH2;
 #define GSCAN_GEN_CT(TX, MTV, NTV)                                                              \
     hipLaunchKernelGGL((gscan_gen_contract_kernel<TX, MTV, NTV>), grid, dim3(kCtThreads), 0, st, \
-                       j0, j1, nb0, d, sh2, part)
+                       j0, j1, d, sh2, part)
     if (p.dtype == 1) {
         if (MT == 256 && NT == 128) GSCAN_GEN_CT(uint16_t, 256, 128);
         else if (MT == 256) GSCAN_GEN_CT(uint16_t, 256, 64);

@@ -1594,6 +1594,32 @@ rows_pass(const TIn *__restrict__ hh, const TIn *__restrict__ hs2, const float *
     }
     accC[0] = zero4();
     accC[1] = zero4();
+    // The plain backward contracts a chunk's rows during the next chunk's
+    // split and projection (PIPE): the contraction's products then issue
+    // beside the split's vector work instead of in a phase of their own.
+    // The chunk's [dA | dB] operands wait in registers, its split rows in
+    // the wavefront's transposition tile, and the 16-column i-tiles 2u and
+    // 2u + 1 are contracted just before unit u of the next chunk overwrites
+    // them (LDS operations of one wavefront execute in order).  Before the
+    // first chunk both the operands and the tile are zero.
+    constexpr bool PIPE = !FWD && !DIN;
+    GradOp pgA, pgB;
+    pgA.b1 = pgA.b2 = pgB.b1 = pgB.b2 = zero_u4();
+    const uint16_t *const trp = tile + (4 * kg + (ln >> 2)) * kPitch + 4 * (ln & 3);
+    // contraction of i-tile tl of the rows in the tile against (gA, gB)
+    auto contract_tile = [&](int tl, const GradOp &gA, const GradOp &gB)
+                             __attribute__((always_inline)) {
+        const uint2 h = read_tr(trp + 16 * tl);
+        u4 av;
+        if constexpr (LO) {
+            const uint2 l = read_tr(trp + 16 * kPitch + 16 * tl);
+            av = u4{h.x, h.y, l.x, l.y};
+        } else {
+            av = u4{h.x, h.y, h.x, h.y};
+        }
+        accA[tl] = contract_op<LO>(av, gA, accA[tl]);
+        accB[tl] = contract_op<LO>(av, gB, accB[tl]);
+    };
 
     auto samples_of = [&](int64_t gg) {
         return (int)(B - gg * kGroupSamples < kGroupSamples ? B - gg * kGroupSamples
@@ -1704,6 +1730,10 @@ rows_pass(const TIn *__restrict__ hh, const TIn *__restrict__ hs2, const float *
             if (u + 1 < NH) {
                 wAn = wop(Wl, half * NH + u + 1, 0, lane);
                 wBn = wop(Wl, half * NH + u + 1, 1, lane);
+            }
+            if constexpr (PIPE) {
+                contract_tile(2 * u, pgA, pgB);
+                contract_tile(2 * u + 1, pgA, pgB);
             }
             const Split sp = pb.op(u);
             pb.load_unit(nrow, kg, u);
@@ -1896,20 +1926,15 @@ rows_pass(const TIn *__restrict__ hh, const TIn *__restrict__ hs2, const float *
         }
         // weight-gradient contraction of this half over the block's 16 rows
         const GradOp gA = grad_op<LO>(dA4), gB = grad_op<LO>(dB4);
-        const uint16_t *const trp = tile + (4 * kg + (ln >> 2)) * kPitch + 4 * (ln & 3);
+        if constexpr (PIPE) {
+            pgA = gA;  // contracted during the next chunk's split
+            pgB = gB;
+        } else {
 #pragma unroll
-        for (int tl = 0; tl < NQ; ++tl) {
-            const uint2 h = read_tr(trp + 16 * tl);
-            u4 av;
-            if constexpr (LO) {
-                const uint2 l = read_tr(trp + 16 * kPitch + 16 * tl);
-                av = u4{h.x, h.y, l.x, l.y};
-            } else {
-                av = u4{h.x, h.y, h.x, h.y};
+            for (int tl = 0; tl < NQ; ++tl) {
+                contract_tile(tl, gA, gB);
+                if (tl % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounded read-ahead
             }
-            accA[tl] = contract_op<LO>(av, gA, accA[tl]);
-            accB[tl] = contract_op<LO>(av, gB, accB[tl]);
-            if (tl % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounded read-ahead
         }
 
         if constexpr (DIN) {
@@ -2054,6 +2079,12 @@ rows_pass(const TIn *__restrict__ hh, const TIn *__restrict__ hs2, const float *
         for (int u = kPre; u < NH; ++u) pA.load_unit(chunk_row(t0), kg, u);
     }
     __syncthreads();  // weights staged
+    if constexpr (PIPE) {
+        // the tile held the raw weights: zero it for the first chunk's
+        // (empty) pending contraction
+        for (int e = lane; e < kTile / 8; e += kWave)
+            reinterpret_cast<u4 *>(tile)[e] = zero_u4();
+    }
     if (cur.g < groups) use_group(samples_of(cur.g));
     while (cur.g < groups) {
         const BTask nxt = advance(cur);
@@ -2061,6 +2092,10 @@ rows_pass(const TIn *__restrict__ hh, const TIn *__restrict__ hs2, const float *
         cur = nxt;
     }
     if constexpr (FWD) return;
+    if constexpr (PIPE) {
+#pragma unroll
+        for (int tl = 0; tl < NQ; ++tl) contract_tile(tl, pgA, pgB);
+    }
 
     // sums over the four blocks of each half: (b0 + b2) + (b1 + b3), in LDS
     // (over the transposition tiles, once every wavefront is done with its

@@ -2516,7 +2516,7 @@ constexpr int kCtRows = 32;
 // WHICH0: the partial the first output column goes to (0: dW_A, then dW_B;
 // 2: dW_C), fixed at compile time so that the two launches are told apart
 // in profiles.
-template <typename TX, int MT, int NT, int WN>
+template <typename TX, int MT, int NT, int WN, bool OVL>
 __device__ __forceinline__ void
 contract_slab(const TX *__restrict__ X, int ldx, const float *__restrict__ Y, int ldy,
               int64_t rows, int64_t rows_per_slab, int D, int SH2, float *__restrict__ part,
@@ -2636,11 +2636,18 @@ contract_slab(const TX *__restrict__ X, int ldx, const float *__restrict__ Y, in
             for (int j = 0; j < NTW; ++j) acc[i][j] = mfma3<LO>(ao, bo[j], acc[i][j]);
         }
     };
-    // step k: its rows (register set k % 2) go to LDS buffer k % 2, the
+    // OVL: step k contracts LDS buffer k % 2 and, in the same stretch,
+    // splits the rows of step k + 1 (register set (k + 1) % 2) into the
+    // other buffer, so that the split's vector work issues beside the
+    // products; the set then takes the rows of step k + 3.  The barrier at
+    // the end of step k publishes buffer (k + 1) % 2 and closes the reads of
+    // buffer k % 2, which step k + 1 refills.  Its extra barrier before the
+    // first step costs more than the overlap gains on short slabs, where
+    // step k instead splits its own rows (set k % 2) into buffer k % 2, the
     // barrier publishes them (and closes the reads of step k - 1), the set
     // takes the rows of step k + 2, and the buffer is contracted.  Rows past
     // the slab load as zeros.
-    if (r_begin < r_end) {
+    if (!OVL && r_begin < r_end) {
         load(0, r_begin);
         load(1, r_begin + kCtRows);
         for (int64_t rb = r_begin; rb < r_end; rb += 2 * kCtRows) {
@@ -2653,6 +2660,24 @@ contract_slab(const TX *__restrict__ X, int ldx, const float *__restrict__ Y, in
             __syncthreads();
             load(1, rb + 3 * kCtRows);
             contract(1);
+        }
+    }
+    if (OVL && r_begin < r_end) {
+        load(0, r_begin);
+        load(1, r_begin + kCtRows);
+        store(0, 0);
+        load(0, r_begin + 2 * kCtRows);
+        __syncthreads();
+        for (int64_t rb = r_begin; rb < r_end; rb += 2 * kCtRows) {
+            store(1, 1);
+            load(1, rb + 3 * kCtRows);
+            contract(0);
+            __syncthreads();
+            if (rb + kCtRows >= r_end) break;
+            store(0, 0);
+            load(0, rb + 4 * kCtRows);
+            contract(1);
+            __syncthreads();
         }
     }
     // partial of this slab: lane l holds i = m-tile row 4(l/16) + e, o = l % 16.
@@ -2681,8 +2706,8 @@ gscan_bwd_contract_kernel(const TX *__restrict__ X, int ldx, const float *__rest
                           int64_t rows, int64_t rows_per_slab, int D, int SH2,
                           float *__restrict__ part)
 {
-    contract_slab<TX, MT, NT, WN>(X, ldx, Y, ldy, rows, rows_per_slab, D, SH2, part, WHICH0,
-                                  blockIdx.x, blockIdx.y, blockIdx.z);
+    contract_slab<TX, MT, NT, WN, true>(X, ldx, Y, ldy, rows, rows_per_slab, D, SH2, part, WHICH0,
+                                        blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Both contractions of the materialised-projection path in one launch, on
@@ -2708,11 +2733,11 @@ gscan_gen_contract_kernel(CtJob j0, CtJob j1, int D, int SH2, float *__restrict_
     const int64_t slab = blockIdx.x / per;
     const int r = (int)(blockIdx.x - slab * per);
     const int mt = r / j0.gn, nt = r % j0.gn;
-    contract_slab<TX, MT, NT, 4>(static_cast<const TX *>(j0.X), j0.ldx, j0.Y, j0.ldy, j0.rows,
+    contract_slab<TX, MT, NT, 4, false>(static_cast<const TX *>(j0.X), j0.ldx, j0.Y, j0.ldy, j0.rows,
                                  j0.rps, D, SH2, part, j0.which0, slab, mt, nt);
     if (nt < j1.gn) {  // the same for every thread of the workgroup
         __syncthreads();  // the tiles' LDS buffers are read to the end first
-        contract_slab<TX, MT, NT, 4>(static_cast<const TX *>(j1.X), j1.ldx, j1.Y, j1.ldy,
+        contract_slab<TX, MT, NT, 4, false>(static_cast<const TX *>(j1.X), j1.ldx, j1.Y, j1.ldy,
                                      j1.rows, j1.rps, D, SH2, part, j1.which0, slab, mt, nt);
     }
 }

@@ -166,6 +166,12 @@ template <int NQ> struct PBlk<float, NQ> {
         v[q][0] = *reinterpret_cast<const f4 *>(row + 32 * q + 8 * kg);
         v[q][1] = *reinterpret_cast<const f4 *>(row + 32 * q + 8 * kg + 4);
     }
+    // unit u of the row into register slot j (a ring of fewer slots than units)
+    __device__ __forceinline__ void load_unit_at(const float *__restrict__ row, int kg, int u, int j)
+    {
+        v[j][0] = *reinterpret_cast<const f4 *>(row + 32 * u + 8 * kg);
+        v[j][1] = *reinterpret_cast<const f4 *>(row + 32 * u + 8 * kg + 4);
+    }
     __device__ __forceinline__ void load(const float *__restrict__ row, int kg)
     {
 #pragma unroll
@@ -185,6 +191,10 @@ template <int NQ> struct PBlk<uint16_t, NQ> {
     __device__ __forceinline__ void load_unit(const uint16_t *__restrict__ row, int kg, int q)
     {
         v[q] = *reinterpret_cast<const u4 *>(row + 32 * q + 8 * kg);
+    }
+    __device__ __forceinline__ void load_unit_at(const uint16_t *__restrict__ row, int kg, int u, int j)
+    {
+        v[j] = *reinterpret_cast<const u4 *>(row + 32 * u + 8 * kg);
     }
     __device__ __forceinline__ void load(const uint16_t *__restrict__ row, int kg)
     {
@@ -843,8 +853,29 @@ gscan_fwd_ms_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     // C values: h_s2 units q = wt + 4i of the group against the C image
     CvLoad<TIn, NQ> cvl;
     cvl.load(hs2 + b0 * SH2 + (uint32_t)((ln < nb ? ln : nb - 1) * SH2), wt, kg);
+    // Two 16-row blocks (32 rows) per pass: each weight operand read from
+    // LDS feeds the products of both blocks, halving the LDS traffic per
+    // row.  The rows wait in a ring of R register slots per block: slot
+    // (q % R) holds unit q, and as soon as a unit has been split its slot
+    // takes the next unit that maps to it (unit q + R of this pair, or a unit
+    // of the next pair), so R < NQ slots keep R units of lead on every load.
+    // The first pair's first R units go out before the weight staging.
+    // With SH2 > 256 (NQ > 8) the second block's accumulators and ring do
+    // not fit beside the rest in 256 registers: one block per pass there,
+    // its rows in one buffer of NQ units refilled with the next block's.
+    constexpr bool TWO = NQ <= 8;
+    constexpr int R = NQ == 8 ? 4 : NQ;
+    PBlk<TIn, R> r0, r1;
     PBlk<TIn, NQ> blk;
-    blk.load(rowp(lr_begin), kg);
+    if constexpr (TWO) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            r0.load_unit_at(rowp(lr_begin), kg, u, u);
+            r1.load_unit_at(rowp(lr_begin + kBlockRows), kg, u, u);
+        }
+    } else {
+        blk.load(rowp(lr_begin), kg);
+    }
     stage_image<NQ, S, 1>(img, WC, WC, D, s0);
     __syncthreads();
     f4 cp[S];
@@ -876,70 +907,164 @@ gscan_fwd_ms_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     __syncthreads();
     if (!gvalid || lr_begin >= lr_end) return;
 
-    float xc[S];
+    if constexpr (TWO) {
+        float xc[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) xc[s] = 0.f;
-    for (int base = lr_begin; base < lr_end; base += kBlockRows) {
-        // the next block's rows (clamped past the end) replace this block's
-        // unit by unit
-        const TIn *__restrict__ nrow = rowp(base + kBlockRows);
-        f4 aA[S], aB[S];
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            aA[s] = zero4();
-            aB[s] = zero4();
-        }
-        // unit q + 1 is split (and its register slot refilled with the next
-        // block's unit) in the same stretch as unit q's products, so the
-        // split's vector work can issue while the matrix cores run
-        Split hn = blk.op(0);
-        blk.load_unit(nrow, kg, 0);
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const Split h = hn;
-            if (q + 1 < NQ) {
-                hn = blk.op(q + 1);
-                blk.load_unit(nrow, kg, q + 1);
-            }
+        for (int s = 0; s < S; ++s) xc[s] = 0.f;
+        for (int base = lr_begin; base < lr_end; base += 2 * kBlockRows) {
+            const TIn *__restrict__ row0 = rowp(base), *__restrict__ row1 = rowp(base + kBlockRows);
+            // the next pair's rows (clamped past the end)
+            const TIn *__restrict__ nrow0 = rowp(base + 2 * kBlockRows);
+            const TIn *__restrict__ nrow1 = rowp(base + 3 * kBlockRows);
+            // slot (u % R) is free once unit u is split: it takes unit u + R of
+            // this pair, or unit u + R - NQ of the next
+            auto refill = [&](int u) __attribute__((always_inline)) {
+                const int n = u + R;
+                if (n < NQ) {
+                    r0.load_unit_at(row0, kg, n, u % R);
+                    r1.load_unit_at(row1, kg, n, u % R);
+                } else {
+                    r0.load_unit_at(nrow0, kg, n - NQ, u % R);
+                    r1.load_unit_at(nrow1, kg, n - NQ, u % R);
+                }
+            };
+            f4 aA0[S], aB0[S], aA1[S], aB1[S];
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                aA[s] = mfma3<LO>(h, img_op(img, (s * NQ + q) * 2, lane), aA[s]);
-                aB[s] = mfma3<LO>(h, img_op(img, (s * NQ + q) * 2 + 1, lane), aB[s]);
+                aA0[s] = zero4();
+                aB0[s] = zero4();
+                aA1[s] = zero4();
+                aB1[s] = zero4();
             }
-            // keep later units' operand reads from being hoisted further
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const RowPos bp = base_pos(base, K);
+            // unit q + 1 is split (and its slot refilled) in the same stretch as
+            // unit q's products, so the split's vector work can issue while the
+            // matrix cores run
+            Split h0n = r0.op(0), h1n = r1.op(0);
+            refill(0);
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            Aff map[4];
-            Aff F = aff_id();
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = base + 4 * kg + j;
-                Aff m;
-                if (r >= lr_end) {
-                    m = aff_id();
-                } else {
-                    m.m = sigmoid(aA[s][j] + a_shift);
-                    m.c = aB[s][j];
-                    m.r = row_pos(bp, lo, j, K).t == 0;
+            for (int q = 0; q < NQ; ++q) {
+                const Split h0 = h0n, h1 = h1n;
+                if (q + 1 < NQ) {
+                    h0n = r0.op((q + 1) % R);
+                    h1n = r1.op((q + 1) % R);
+                    refill(q + 1);
                 }
-                map[j] = m;
-                F = compose(m, F);
-            }
-            Aff excl, total;
-            scan_up(F, lane, excl, total);
-            float x = apply(excl, xc[s]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                x = apply(map[j], x);
-                const int r = base + 4 * kg + j;
-                const RowPos rp = row_pos(bp, lo, j, K);
-                if (r < lr_end && rp.t == K - 1)
-                    put_context(out, b0 + rp.bl, D, s0 + 16 * s + ln, cvs[team][s][rp.bl][ln] * x);
+                for (int s = 0; s < S; ++s) {
+                    const Split wa = img_op(img, (s * NQ + q) * 2, lane);
+                    const Split wb = img_op(img, (s * NQ + q) * 2 + 1, lane);
+                    aA0[s] = mfma3<LO>(h0, wa, aA0[s]);
+                    aA1[s] = mfma3<LO>(h1, wa, aA1[s]);
+                    aB0[s] = mfma3<LO>(h0, wb, aB0[s]);
+                    aB1[s] = mfma3<LO>(h1, wb, aB1[s]);
+                }
+                // keep later units' operand reads from being hoisted further
+                __builtin_amdgcn_sched_barrier(0);
             }
-            xc[s] = apply(total, xc[s]);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int bb = base + kBlockRows * hb;
+                const RowPos bp = base_pos(bb, K);
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const f4 pa = hb ? aA1[s] : aA0[s], pbv = hb ? aB1[s] : aB0[s];
+                    Aff map[4];
+                    Aff F = aff_id();
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = bb + 4 * kg + j;
+                        Aff m;
+                        if (r >= lr_end) {
+                            m = aff_id();
+                        } else {
+                            m.m = sigmoid(pa[j] + a_shift);
+                            m.c = pbv[j];
+                            m.r = row_pos(bp, lo, j, K).t == 0;
+                        }
+                        map[j] = m;
+                        F = compose(m, F);
+                    }
+                    Aff excl, total;
+                    scan_up(F, lane, excl, total);
+                    float x = apply(excl, xc[s]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        x = apply(map[j], x);
+                        const int r = bb + 4 * kg + j;
+                        const RowPos rp = row_pos(bp, lo, j, K);
+                        if (r < lr_end && rp.t == K - 1)
+                            put_context(out, b0 + rp.bl, D, s0 + 16 * s + ln, cvs[team][s][rp.bl][ln] * x);
+                    }
+                    xc[s] = apply(total, xc[s]);
+                }
+            }
+        }
+    } else {
+        float xc[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) xc[s] = 0.f;
+        for (int base = lr_begin; base < lr_end; base += kBlockRows) {
+            // the next block's rows (clamped past the end) replace this block's
+            // unit by unit
+            const TIn *__restrict__ nrow = rowp(base + kBlockRows);
+            f4 aA[S], aB[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                aA[s] = zero4();
+                aB[s] = zero4();
+            }
+            // unit q + 1 is split (and its register slot refilled with the next
+            // block's unit) in the same stretch as unit q's products, so the
+            // split's vector work can issue while the matrix cores run
+            Split hn = blk.op(0);
+            blk.load_unit(nrow, kg, 0);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const Split h = hn;
+                if (q + 1 < NQ) {
+                    hn = blk.op(q + 1);
+                    blk.load_unit(nrow, kg, q + 1);
+                }
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    aA[s] = mfma3<LO>(h, img_op(img, (s * NQ + q) * 2, lane), aA[s]);
+                    aB[s] = mfma3<LO>(h, img_op(img, (s * NQ + q) * 2 + 1, lane), aB[s]);
+                }
+                // keep later units' operand reads from being hoisted further
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const RowPos bp = base_pos(base, K);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                Aff map[4];
+                Aff F = aff_id();
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = base + 4 * kg + j;
+                    Aff m;
+                    if (r >= lr_end) {
+                        m = aff_id();
+                    } else {
+                        m.m = sigmoid(aA[s][j] + a_shift);
+                        m.c = aB[s][j];
+                        m.r = row_pos(bp, lo, j, K).t == 0;
+                    }
+                    map[j] = m;
+                    F = compose(m, F);
+                }
+                Aff excl, total;
+                scan_up(F, lane, excl, total);
+                float x = apply(excl, xc[s]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x = apply(map[j], x);
+                    const int r = base + 4 * kg + j;
+                    const RowPos rp = row_pos(bp, lo, j, K);
+                    if (r < lr_end && rp.t == K - 1)
+                        put_context(out, b0 + rp.bl, D, s0 + 16 * s + ln, cvs[team][s][rp.bl][ln] * x);
+                }
+                xc[s] = apply(total, xc[s]);
+            }
         }
     }
 }

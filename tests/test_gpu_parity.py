@@ -62,6 +62,16 @@ SMALL = [
     (40, 16, 256, 64, "bf16", 0.5),
     (33, 20, 384, 32, "f32", -0.5),
     (9000, 16, 64, 32, "f32", 1.0),
+    # D > 16 with SH2 <= 256: the multi-slice forward takes two row blocks
+    # per pass (a ring of four units per block at SH2 = 256, whole blocks
+    # below), including a last pair whose second block is partly or wholly
+    # past a wavefront's rows (4K not a multiple of 32)
+    (40, 16, 256, 32, "f32", 0.75),
+    (37, 24, 192, 64, "f32", -1.5),
+    (33, 5, 128, 64, "f32", 1.0),
+    (9, 64, 256, 64, "bf16", 2.0),
+    (21, 3, 64, 32, "bf16", 0.0),
+    (300, 17, 256, 64, "f32", 0.5),
     # K = 32 or 64 with SH2 <= 256 (the per-block backward kernel): a sample
     # fills 2 or 4 blocks of a chunk
     (21, 32, 128, 16, "f32", 0.0),

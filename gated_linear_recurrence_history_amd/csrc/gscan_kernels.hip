@@ -767,9 +767,8 @@ gscan_fwd_persist_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2
 // 32-column unit of a row block is split once and multiplied with the A and
 // B weights of all S slices, held in LDS as one bf16 hi/lo image (S * SH2 *
 // 32 pairs, at most 128 KiB).  The C weights pass through the same LDS first,
-// for the C values of both groups.  The next block's unit q is requested as
-// soon as unit q of the current block has been split, so one register buffer
-// holds both blocks.
+// for the C values of both groups.  Each wavefront takes two 16-row blocks
+// per pass, so that every weight operand read from LDS serves both.
 constexpr int kWavesM = 8;
 constexpr int kThreadsM = kWave * kWavesM;
 
@@ -860,21 +859,15 @@ gscan_fwd_ms_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     // takes the next unit that maps to it (unit q + R of this pair, or a unit
     // of the next pair), so R < NQ slots keep R units of lead on every load.
     // The first pair's first R units go out before the weight staging.
-    // With SH2 > 256 (NQ > 8) the second block's accumulators and ring do
-    // not fit beside the rest in 256 registers: one block per pass there,
-    // its rows in one buffer of NQ units refilled with the next block's.
-    constexpr bool TWO = NQ <= 8;
-    constexpr int R = NQ == 8 ? 4 : NQ;
+    // R divides NQ (a slot holds units q, q + R, ...): four where it can,
+    // whole blocks for SH2 <= 192.
+    constexpr int R = NQ % 4 == 0 && NQ >= 8 ? 4 : (NQ == 10 ? 5 : (NQ == 14 ? 7 : NQ));
+    static_assert(NQ % R == 0, "ring slots");
     PBlk<TIn, R> r0, r1;
-    PBlk<TIn, NQ> blk;
-    if constexpr (TWO) {
 #pragma unroll
-        for (int u = 0; u < R; ++u) {
-            r0.load_unit_at(rowp(lr_begin), kg, u, u);
-            r1.load_unit_at(rowp(lr_begin + kBlockRows), kg, u, u);
-        }
-    } else {
-        blk.load(rowp(lr_begin), kg);
+    for (int u = 0; u < R; ++u) {
+        r0.load_unit_at(rowp(lr_begin), kg, u, u);
+        r1.load_unit_at(rowp(lr_begin + kBlockRows), kg, u, u);
     }
     stage_image<NQ, S, 1>(img, WC, WC, D, s0);
     __syncthreads();
@@ -907,146 +900,77 @@ gscan_fwd_ms_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
     __syncthreads();
     if (!gvalid || lr_begin >= lr_end) return;
 
-    if constexpr (TWO) {
-        float xc[S];
+    float xc[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) xc[s] = 0.f;
-        for (int base = lr_begin; base < lr_end; base += 2 * kBlockRows) {
-            const TIn *__restrict__ row0 = rowp(base), *__restrict__ row1 = rowp(base + kBlockRows);
-            // the next pair's rows (clamped past the end)
-            const TIn *__restrict__ nrow0 = rowp(base + 2 * kBlockRows);
-            const TIn *__restrict__ nrow1 = rowp(base + 3 * kBlockRows);
-            // slot (u % R) is free once unit u is split: it takes unit u + R of
-            // this pair, or unit u + R - NQ of the next
-            auto refill = [&](int u) __attribute__((always_inline)) {
-                const int n = u + R;
-                if (n < NQ) {
-                    r0.load_unit_at(row0, kg, n, u % R);
-                    r1.load_unit_at(row1, kg, n, u % R);
-                } else {
-                    r0.load_unit_at(nrow0, kg, n - NQ, u % R);
-                    r1.load_unit_at(nrow1, kg, n - NQ, u % R);
-                }
-            };
-            f4 aA0[S], aB0[S], aA1[S], aB1[S];
-#pragma unroll
-            for (int s = 0; s < S; ++s) {
-                aA0[s] = zero4();
-                aB0[s] = zero4();
-                aA1[s] = zero4();
-                aB1[s] = zero4();
+    for (int s = 0; s < S; ++s) xc[s] = 0.f;
+    for (int base = lr_begin; base < lr_end; base += 2 * kBlockRows) {
+        const TIn *__restrict__ row0 = rowp(base), *__restrict__ row1 = rowp(base + kBlockRows);
+        // the next pair's rows (clamped past the end)
+        const TIn *__restrict__ nrow0 = rowp(base + 2 * kBlockRows);
+        const TIn *__restrict__ nrow1 = rowp(base + 3 * kBlockRows);
+        // slot (u % R) is free once unit u is split: it takes unit u + R of
+        // this pair, or unit u + R - NQ of the next
+        auto refill = [&](int u) __attribute__((always_inline)) {
+            const int n = u + R;
+            if (n < NQ) {
+                r0.load_unit_at(row0, kg, n, u % R);
+                r1.load_unit_at(row1, kg, n, u % R);
+            } else {
+                r0.load_unit_at(nrow0, kg, n - NQ, u % R);
+                r1.load_unit_at(nrow1, kg, n - NQ, u % R);
             }
-            // unit q + 1 is split (and its slot refilled) in the same stretch as
-            // unit q's products, so the split's vector work can issue while the
-            // matrix cores run
-            Split h0n = r0.op(0), h1n = r1.op(0);
-            refill(0);
+        };
+        f4 aA0[S], aB0[S], aA1[S], aB1[S];
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                const Split h0 = h0n, h1 = h1n;
-                if (q + 1 < NQ) {
-                    h0n = r0.op((q + 1) % R);
-                    h1n = r1.op((q + 1) % R);
-                    refill(q + 1);
-                }
-#pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    const Split wa = img_op(img, (s * NQ + q) * 2, lane);
-                    const Split wb = img_op(img, (s * NQ + q) * 2 + 1, lane);
-                    aA0[s] = mfma3<LO>(h0, wa, aA0[s]);
-                    aA1[s] = mfma3<LO>(h1, wa, aA1[s]);
-                    aB0[s] = mfma3<LO>(h0, wb, aB0[s]);
-                    aB1[s] = mfma3<LO>(h1, wb, aB1[s]);
-                }
-                // keep later units' operand reads from being hoisted further
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                const int bb = base + kBlockRows * hb;
-                const RowPos bp = base_pos(bb, K);
-#pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    const f4 pa = hb ? aA1[s] : aA0[s], pbv = hb ? aB1[s] : aB0[s];
-                    Aff map[4];
-                    Aff F = aff_id();
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = bb + 4 * kg + j;
-                        Aff m;
-                        if (r >= lr_end) {
-                            m = aff_id();
-                        } else {
-                            m.m = sigmoid(pa[j] + a_shift);
-                            m.c = pbv[j];
-                            m.r = row_pos(bp, lo, j, K).t == 0;
-                        }
-                        map[j] = m;
-                        F = compose(m, F);
-                    }
-                    Aff excl, total;
-                    scan_up(F, lane, excl, total);
-                    float x = apply(excl, xc[s]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        x = apply(map[j], x);
-                        const int r = bb + 4 * kg + j;
-                        const RowPos rp = row_pos(bp, lo, j, K);
-                        if (r < lr_end && rp.t == K - 1)
-                            put_context(out, b0 + rp.bl, D, s0 + 16 * s + ln, cvs[team][s][rp.bl][ln] * x);
-                    }
-                    xc[s] = apply(total, xc[s]);
-                }
-            }
+        for (int s = 0; s < S; ++s) {
+            aA0[s] = zero4();
+            aB0[s] = zero4();
+            aA1[s] = zero4();
+            aB1[s] = zero4();
         }
-    } else {
-        float xc[S];
+        // unit q + 1 is split (and its slot refilled) in the same stretch as
+        // unit q's products, so the split's vector work can issue while the
+        // matrix cores run
+        Split h0n = r0.op(0), h1n = r1.op(0);
+        refill(0);
 #pragma unroll
-        for (int s = 0; s < S; ++s) xc[s] = 0.f;
-        for (int base = lr_begin; base < lr_end; base += kBlockRows) {
-            // the next block's rows (clamped past the end) replace this block's
-            // unit by unit
-            const TIn *__restrict__ nrow = rowp(base + kBlockRows);
-            f4 aA[S], aB[S];
+        for (int q = 0; q < NQ; ++q) {
+            const Split h0 = h0n, h1 = h1n;
+            if (q + 1 < NQ) {
+                h0n = r0.op((q + 1) % R);
+                h1n = r1.op((q + 1) % R);
+                refill(q + 1);
+            }
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                aA[s] = zero4();
-                aB[s] = zero4();
+                const Split wa = img_op(img, (s * NQ + q) * 2, lane);
+                const Split wb = img_op(img, (s * NQ + q) * 2 + 1, lane);
+                aA0[s] = mfma3<LO>(h0, wa, aA0[s]);
+                aA1[s] = mfma3<LO>(h1, wa, aA1[s]);
+                aB0[s] = mfma3<LO>(h0, wb, aB0[s]);
+                aB1[s] = mfma3<LO>(h1, wb, aB1[s]);
             }
-            // unit q + 1 is split (and its register slot refilled with the next
-            // block's unit) in the same stretch as unit q's products, so the
-            // split's vector work can issue while the matrix cores run
-            Split hn = blk.op(0);
-            blk.load_unit(nrow, kg, 0);
+            // keep later units' operand reads from being hoisted further
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                const Split h = hn;
-                if (q + 1 < NQ) {
-                    hn = blk.op(q + 1);
-                    blk.load_unit(nrow, kg, q + 1);
-                }
-#pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    aA[s] = mfma3<LO>(h, img_op(img, (s * NQ + q) * 2, lane), aA[s]);
-                    aB[s] = mfma3<LO>(h, img_op(img, (s * NQ + q) * 2 + 1, lane), aB[s]);
-                }
-                // keep later units' operand reads from being hoisted further
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const RowPos bp = base_pos(base, K);
+        for (int hb = 0; hb < 2; ++hb) {
+            const int bb = base + kBlockRows * hb;
+            const RowPos bp = base_pos(bb, K);
 #pragma unroll
             for (int s = 0; s < S; ++s) {
+                const f4 pa = hb ? aA1[s] : aA0[s], pbv = hb ? aB1[s] : aB0[s];
                 Aff map[4];
                 Aff F = aff_id();
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = base + 4 * kg + j;
+                    const int r = bb + 4 * kg + j;
                     Aff m;
                     if (r >= lr_end) {
                         m = aff_id();
                     } else {
-                        m.m = sigmoid(aA[s][j] + a_shift);
-                        m.c = aB[s][j];
+                        m.m = sigmoid(pa[j] + a_shift);
+                        m.c = pbv[j];
                         m.r = row_pos(bp, lo, j, K).t == 0;
                     }
                     map[j] = m;
@@ -1058,7 +982,7 @@ gscan_fwd_ms_kernel(const TIn *__restrict__ hh, const TIn *__restrict__ hs2,
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     x = apply(map[j], x);
-                    const int r = base + 4 * kg + j;
+                    const int r = bb + 4 * kg + j;
                     const RowPos rp = row_pos(bp, lo, j, K);
                     if (r < lr_end && rp.t == K - 1)
                         put_context(out, b0 + rp.bl, D, s0 + 16 * s + ln, cvs[team][s][rp.bl][ln] * x);

@@ -5,7 +5,8 @@ input values copied into the captured buffers, eager work and
 synchronisations between the replays; every replay is compared bitwise
 with the same calls made eagerly on the same inputs.  Nothing in these
 calls allocates or clears memory from the host, so the captured graph
-holds kernel nodes only."""
+holds kernel nodes only (SH2 = 208 runs the materialised-projection path,
+whose forward also takes a caller workspace here)."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +19,7 @@ pytestmark = pytest.mark.gpu
 from tests.gpu_util import DEV, device_inputs, workload  # noqa: E402
 
 
-@pytest.mark.parametrize("shape", [(512, 8, 256, 16), (300, 5, 192, 32)],
+@pytest.mark.parametrize("shape", [(512, 8, 256, 16), (300, 5, 192, 32), (300, 5, 208, 32)],
                          ids=lambda s: "B%d_K%d_S%d_D%d" % s)
 def test_graph_replay_matches_eager(shape):
     B, K, SH2, D = shape
@@ -29,11 +30,13 @@ def test_graph_replay_matches_eager(shape):
     dW = tuple(torch.empty((SH2, D), device=DEV) for _ in range(3))
     dW_na = tuple(torch.empty((SH2, D), device=DEV) for _ in range(3))
     ws = torch.empty(gs.backward_workspace_bytes(B, K, SH2, D), dtype=torch.uint8, device=DEV)
+    nf = gs.forward_workspace_bytes(B, K, SH2, D)
+    wsf = torch.empty(nf, dtype=torch.uint8, device=DEV) if nf else None
     args = (t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], K)
     L = binding.lib()
 
     def step():
-        gs.forward(*args, 0.5, out=ctx)
+        gs.forward(*args, 0.5, out=ctx, workspace=wsf)
         gs.backward(*args, t["d_context"], 0.5, out=dW, workspace=ws)
         stream = torch.cuda.current_stream(DEV).cuda_stream
         ptr = [a.data_ptr() for a in args[:5]]
